@@ -1,0 +1,190 @@
+"""Block-scaled FP8 GEMMs and the output acceptance rule -- oracle.
+
+tmdrlife.com wr_id=13334 ¶3 and gnrental.net wr_id=40936 ¶4: once the
+accumulation interval is reached, the partial products are moved to FP32
+registers, multiplied by the scaling factors and added there.
+jp-study.kr doc 258368 ¶3: that interval is 128 elements of K.  Since each
+128-element K interval is one activation tile and one weight block, the
+result the method reaches (up to rounding order) has the plain definition
+
+    C[m, n] = sum_b  sa[m, b] * sw[n // 128, b] * sum_{k in block b} qa[m, k] * qw[n, k]
+
+with qa, qw the decoded E4M3 values.  That definition is written out here.
+Every E4M3 value is an integer multiple of 2^-9 with magnitude below 2^18 *
+2^-9, so each block's partial sum is an integer multiple of 2^-18 below 2^25
+in magnitude: it is exact in float64 whatever the summation order.  The scale
+product of two float32 values is exact in float64 (48 significant bits).
+Only the outer sum over blocks rounds, by at most about n_blocks * 2^-53
+relative to S below.
+
+S[m, n] = sum_b |sa * sw| * sum_k |qa| * |qw| is the sum of |a_i * b_i| over
+the dequantized operands; the acceptance rule for a GPU result c is
+
+    FP32 output:  |c - C| <= 1e-5 * S + 1e-6
+    BF16 output:  c is the round-to-nearest-even BF16 of some float32 value
+                  in [C - tol, C + tol], tol = 1e-5 * S + 1e-6  (an interval
+                  test, since rounding is monotone)
+
+jp-study.kr doc 258368 ¶3 (Wgrad in FP8): the weight gradient is the same
+contraction over the token axis with both operands scaled per 128 tokens and
+per row, dW[n, c] = sum_b sdy[n, b] * sx[c, b] * sum_{t in b} qdy[n, t] qx[c, t].
+
+Pins: tests/test_oracle_gemm.py (exact integer + Fraction brute force on the
+tiny-linear shape, constant-operand closed form, selector weights, zero
+scales, grouped == per-group dense, Wgrad == dense when scales are constant
+per block, the BF16 interval rule on hand-made cases).
+"""
+
+import numpy as np
+
+from .e4m3 import decode_int
+
+TILE = 128
+TWO_M18 = 2.0 ** -18
+
+
+def _block_partials_int(a_codes, w_codes, b):
+    """Exact per-block partial sums in units of 2^-18, as float64 (exact)."""
+    sl = slice(b * TILE, (b + 1) * TILE)
+    ia = decode_int(a_codes[:, sl]).astype(np.float64)
+    iw = decode_int(w_codes[:, sl]).astype(np.float64)
+    return ia @ iw.T, np.abs(ia) @ np.abs(iw).T
+
+
+def gemm(a_codes, a_scales, w_codes, w_scales):
+    """Dense C = A . W^T with 1x128 activation scales and 128x128 weight scales.
+
+    a_codes [M, K], a_scales [M, K/128], w_codes [N, K],
+    w_scales [ceil(N/128), K/128].  Returns (C, S) as float64 [M, N].
+    """
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    w_codes = np.asarray(w_codes, dtype=np.uint8)
+    m, k = a_codes.shape
+    n = w_codes.shape[0]
+    if k % TILE:
+        raise ValueError("K must be a multiple of 128")
+    nb = k // TILE
+    sa = np.asarray(a_scales, dtype=np.float32).astype(np.float64)
+    sw = np.repeat(np.asarray(w_scales, dtype=np.float32).astype(np.float64), TILE, axis=0)[:n]
+    c = np.zeros((m, n))
+    s = np.zeros((m, n))
+    for b in range(nb):
+        p, pabs = _block_partials_int(a_codes, w_codes, b)
+        scale = sa[:, b][:, None] * sw[:, b][None, :]  # exact in float64
+        c += scale * (p * TWO_M18)
+        s += np.abs(scale) * (pabs * TWO_M18)
+    return c, s
+
+
+def grouped_gemm(a_codes, a_scales, offsets, w_codes, w_scales):
+    """Per-group dense GEMM: rows [offsets[g], offsets[g+1]) use W[g].
+
+    a_codes [rows, K]; offsets int [G+1]; w_codes [G, N, K];
+    w_scales [G, ceil(N/128), K/128].  Returns (C, S) float64 [rows, N]; rows
+    not covered by any group are NaN.
+    """
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    offsets = [int(v) for v in offsets]
+    g_count = len(offsets) - 1
+    n = np.asarray(w_codes).shape[1]
+    c = np.full((a_codes.shape[0], n), np.nan)
+    s = np.full((a_codes.shape[0], n), np.nan)
+    for g in range(g_count):
+        lo, hi = offsets[g], offsets[g + 1]
+        if hi <= lo:
+            continue
+        cg, sg = gemm(a_codes[lo:hi], np.asarray(a_scales)[lo:hi], w_codes[g], w_scales[g])
+        c[lo:hi] = cg
+        s[lo:hi] = sg
+    return c, s
+
+
+def wgrad(dy_t_codes, dy_scales, x_t_codes, x_scales):
+    """dW = dY^T X over the token axis, both operands 128x1 token tiles.
+
+    dy_t_codes [Nout, T], dy_scales [Nout, T/128], x_t_codes [Kin, T],
+    x_scales [Kin, T/128].  Returns (dW, S) float64 [Nout, Kin].
+    """
+    dy = np.asarray(dy_t_codes, dtype=np.uint8)
+    xt = np.asarray(x_t_codes, dtype=np.uint8)
+    nout, t = dy.shape
+    kin = xt.shape[0]
+    if t % TILE:
+        raise ValueError("T must be a multiple of 128")
+    sdy = np.asarray(dy_scales, dtype=np.float32).astype(np.float64)
+    sx = np.asarray(x_scales, dtype=np.float32).astype(np.float64)
+    c = np.zeros((nout, kin))
+    s = np.zeros((nout, kin))
+    for b in range(t // TILE):
+        p, pabs = _block_partials_int(dy, xt, b)
+        scale = sdy[:, b][:, None] * sx[:, b][None, :]
+        c += scale * (p * TWO_M18)
+        s += np.abs(scale) * (pabs * TWO_M18)
+    return c, s
+
+
+def gemm_at(a_codes, a_scales, w_codes, w_scales, rows, cols, w_block_rows=True):
+    """C and S at sampled positions (rows[i], cols[i]) only, one by one.
+
+    Same definition as ``gemm`` (w_block_rows=True: weight scales per 128-row
+    block) or ``wgrad`` (w_block_rows=False: weight scales per row), evaluated
+    for a list of output elements so full-size problems can be checked.
+    """
+    a_codes = np.asarray(a_codes, dtype=np.uint8)
+    w_codes = np.asarray(w_codes, dtype=np.uint8)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    k = a_codes.shape[1]
+    nb = k // TILE
+    ia = decode_int(a_codes[rows]).astype(np.float64).reshape(-1, nb, TILE)
+    iw = decode_int(w_codes[cols]).astype(np.float64).reshape(-1, nb, TILE)
+    p = np.einsum("ibk,ibk->ib", ia, iw) * TWO_M18  # exact per block
+    pabs = np.einsum("ibk,ibk->ib", np.abs(ia), np.abs(iw)) * TWO_M18
+    sa = np.asarray(a_scales, dtype=np.float32).astype(np.float64)[rows]
+    wr = cols // TILE if w_block_rows else cols
+    sw = np.asarray(w_scales, dtype=np.float32).astype(np.float64)[wr]
+    scale = sa * sw
+    return (scale * p).sum(axis=1), (np.abs(scale) * pabs).sum(axis=1)
+
+
+# ----------------------------------------------------- acceptance rule ----
+
+def tolerance(s):
+    return 1e-5 * np.asarray(s, dtype=np.float64) + 1e-6
+
+
+def accept_f32(c_gpu, c_ref, s_ref):
+    """Elementwise |c_gpu - C| <= 1e-5 * S + 1e-6 (boolean array)."""
+    err = np.abs(np.asarray(c_gpu, dtype=np.float64) - c_ref)
+    return err <= tolerance(s_ref)
+
+
+def _f32_toward(x, up):
+    """Nearest float32 >= x (up=True) or <= x (up=False), for float64 x."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    f64 = f.astype(np.float64)
+    if up:
+        return np.where(f64 < x, np.nextafter(f, np.float32(np.inf)), f)
+    return np.where(f64 > x, np.nextafter(f, np.float32(-np.inf)), f)
+
+
+def _bf16_rne_value(f32):
+    """RNE rounding of float32 values to BF16, returned as float64 values."""
+    u = np.ascontiguousarray(np.asarray(f32, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def accept_bf16(c_gpu_bf16_bits, c_ref, s_ref):
+    """BF16 output rule: c_gpu in [RNE(lo32), RNE(hi32)] (boolean array).
+
+    lo32 / hi32 are the float32 values closest to C -/+ tol from inside the
+    interval, so the accepted set is exactly the BF16 roundings of float32
+    values within tolerance.
+    """
+    tol = tolerance(s_ref)
+    lo = _bf16_rne_value(_f32_toward(c_ref - tol, up=True))
+    hi = _bf16_rne_value(_f32_toward(c_ref + tol, up=False))
+    v = (np.asarray(c_gpu_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    v = v.astype(np.float64)
+    return (v >= lo) & (v <= hi)
