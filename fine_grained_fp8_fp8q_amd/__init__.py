@@ -1,0 +1,248 @@
+"""fine_grained_fp8_fp8q_amd -- fine-grained FP8 (E4M3) linear-layer hot path
+for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libfp8q.so`` (declared in
+``include/fp8q.h``).  Every step of the path runs in the library's HIP
+kernels; this module only checks tensor types, allocates outputs with torch
+(device memory and the current stream are torch's) and marshals arguments.
+There is no fallback: if the library is missing or the device is not gfx950
+the calls raise.
+
+Functions (names follow the C ABI without the ``fp8q_`` prefix):
+
+* ``quantize_act(x, tile_axis="row"|"token_t", scale_mode="free"|"pow2")``
+  -> (codes uint8, scales float32)
+* ``quantize_weight(w, scale_mode="free"|"pow2")`` -> (codes, scales)
+* ``gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16|torch.float32)``
+* ``grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=...)``
+* ``wgrad(dy_t, dy_scales, x_t, x_scales)``
+"""
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8q.so")
+
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_DEVICE = range(6)
+SCALE_FREE, SCALE_POW2 = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+TILE_ROW, TILE_TOKEN_T = 0, 1
+
+SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm", "fp8q_grouped_gemm",
+           "fp8q_wgrad", "fp8q_status_string")
+
+_lib = None
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load_library(path=None):
+    """Load libfp8q.so (built in place by ``build.py``) and declare signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m fine_grained_fp8_fp8q_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.fp8q_quantize_act.argtypes = [vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
+    lib.fp8q_quantize_weight.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp]
+    lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    for name in SYMBOLS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    lib.fp8q_status_string.argtypes = [ctypes.c_int]
+    lib.fp8q_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().fp8q_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != OK:
+        raise Fp8qError(status, where)
+
+
+# ------------------------------------------------------- torch plumbing ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _row_major(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _pad16(n):
+    return (n + 15) // 16 * 16
+
+
+def _scale_mode(mode):
+    return {"free": SCALE_FREE, "pow2": SCALE_POW2}[mode]
+
+
+def _alloc_codes(rows, cols, device):
+    """uint8 [rows, cols] view of a buffer whose row stride is a multiple of 16."""
+    torch = _torch()
+    buf = torch.empty((rows, _pad16(max(cols, 1))), dtype=torch.uint8, device=device)
+    return buf[:, :cols]
+
+
+# ------------------------------------------------------------ the calls ----
+
+def quantize_act(x, tile_axis="row", scale_mode="free"):
+    """BF16 [rows, cols] -> (codes, scales).
+
+    tile_axis="row": 1x128 tiles along cols; codes [rows, cols],
+    scales [rows, ceil(cols/128)].  tile_axis="token_t": 128x1 tiles along
+    rows; codes [cols, rows] (transposed), scales [cols, ceil(rows/128)].
+    """
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    ldx = _row_major(x, "x")
+    rows, cols = x.shape
+    axis = {"row": TILE_ROW, "token_t": TILE_TOKEN_T}[tile_axis]
+    if axis == TILE_ROW:
+        codes = _alloc_codes(rows, cols, x.device)
+        scales = torch.empty((rows, (cols + 127) // 128), dtype=torch.float32, device=x.device)
+    else:
+        codes = _alloc_codes(cols, rows, x.device)
+        scales = torch.empty((cols, (rows + 127) // 128), dtype=torch.float32, device=x.device)
+    st = load_library().fp8q_quantize_act(_ptr(x), rows, cols, ldx, axis, _scale_mode(scale_mode),
+                                          _ptr(codes), codes.stride(0) if codes.numel() else 16,
+                                          _ptr(scales), _stream(x))
+    _check(st, "fp8q_quantize_act")
+    return codes, scales
+
+
+def quantize_weight(w, scale_mode="free"):
+    """BF16 [N, K] -> (codes [N, K], scales [ceil(N/128), ceil(K/128)])."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    ldw = _row_major(w, "w")
+    n, k = w.shape
+    codes = _alloc_codes(n, k, w.device)
+    scales = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32, device=w.device)
+    st = load_library().fp8q_quantize_weight(_ptr(w), n, k, ldw, _scale_mode(scale_mode), _ptr(codes),
+                                             codes.stride(0) if codes.numel() else 16, _ptr(scales),
+                                             _stream(w))
+    _check(st, "fp8q_quantize_weight")
+    return codes, scales
+
+
+def _out_code(dtype):
+    torch = _torch()
+    if dtype == torch.bfloat16:
+        return OUT_BF16
+    if dtype == torch.float32:
+        return OUT_F32
+    raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def _contig_codes(t, name):
+    torch = _torch()
+    _need(t, torch.uint8, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (K-contiguous rows, no padding)")
+
+
+def _contig_f32(t, name):
+    torch = _torch()
+    _need(t, torch.float32, name)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemm(a, a_scales, w, w_scales, out_dtype=None, out=None):
+    """C[M, N] = block-scaled A . W^T from E4M3 codes and float32 scales."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    for t, n in ((a, "a"), (w, "w")):
+        _contig_codes(t, n)
+    for t, n in ((a_scales, "a_scales"), (w_scales, "w_scales")):
+        _contig_f32(t, n)
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k or a_scales.shape != (m, k // 128) or w_scales.shape != ((n + 127) // 128, k // 128):
+        raise ValueError("operand shapes do not match")
+    c = out if out is not None else torch.empty((m, n), dtype=out_dtype, device=a.device)
+    st = load_library().fp8q_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), m, n, k,
+                                  _out_code(c.dtype), _ptr(c), c.stride(0), _stream(a))
+    _check(st, "fp8q_gemm")
+    return c
+
+
+def grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=None, out=None):
+    """Per-expert block-scaled GEMM; rows [offsets[g], offsets[g+1]) use w[g].
+
+    offsets: int32 device tensor [G+1].  Rows of the output not covered by any
+    group are left as allocated (uninitialised unless ``out`` is given).
+    """
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _contig_codes(a, "a")
+    _contig_codes(w, "w")
+    _contig_f32(a_scales, "a_scales")
+    _contig_f32(w_scales, "w_scales")
+    _need(offsets, torch.int32, "offsets")
+    rows_cap, k = a.shape
+    g, n, kw = w.shape
+    if kw != k or offsets.numel() != g + 1:
+        raise ValueError("operand shapes do not match")
+    c = out if out is not None else torch.empty((rows_cap, n), dtype=out_dtype, device=a.device)
+    st = load_library().fp8q_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(offsets), g, rows_cap, _ptr(w),
+                                          _ptr(w_scales), n, k, _out_code(c.dtype), _ptr(c), c.stride(0),
+                                          _stream(a))
+    _check(st, "fp8q_grouped_gemm")
+    return c
+
+
+def wgrad(dy_t, dy_scales, x_t, x_scales, out=None):
+    """dW[Nout, Kin] = dY^T X (float32) from token-axis-quantized operands."""
+    torch = _torch()
+    _contig_codes(dy_t, "dy_t")
+    _contig_codes(x_t, "x_t")
+    _contig_f32(dy_scales, "dy_scales")
+    _contig_f32(x_scales, "x_scales")
+    nout, t = dy_t.shape
+    kin = x_t.shape[0]
+    if x_t.shape[1] != t:
+        raise ValueError("operand shapes do not match")
+    dw = out if out is not None else torch.empty((nout, kin), dtype=torch.float32, device=dy_t.device)
+    st = load_library().fp8q_wgrad(_ptr(dy_t), _ptr(dy_scales), _ptr(x_t), _ptr(x_scales), nout, kin, t,
+                                   _ptr(dw), dw.stride(0), _stream(dy_t))
+    _check(st, "fp8q_wgrad")
+    return dw

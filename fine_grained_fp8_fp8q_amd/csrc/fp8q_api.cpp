@@ -1,0 +1,150 @@
+// C-ABI entry points of libfp8q.so: argument validation, device check and
+// dispatch to the gfx950 kernels.  Every check runs before anything touches
+// the GPU, so an argument error leaves the outputs untouched and launches
+// nothing.
+#include <atomic>
+#include <cstring>
+
+#include "fp8q.h"
+#include "fp8q_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dim_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+fp8q_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8Q_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int cached = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (cached) return cached == 1 ? FP8Q_OK : FP8Q_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8Q_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP8Q_OK : FP8Q_ERR_DEVICE;
+}
+
+fp8q_status launched(hipError_t e) { return e == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_status_string(fp8q_status s) {
+  switch (s) {
+    case FP8Q_OK: return "ok";
+    case FP8Q_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or unknown enum)";
+    case FP8Q_ERR_SHAPE: return "bad shape (leading dimension too small, K not a multiple of 128, or size >= 2^31)";
+    case FP8Q_ERR_ALIGN: return "misaligned base pointer (16-byte alignment required)";
+    case FP8Q_ERR_LAUNCH: return "kernel launch failed";
+    case FP8Q_ERR_DEVICE: return "current device is not an MI355X (gfx950)";
+  }
+  return "unknown status";
+}
+
+fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              int tile_axis, int scale_mode, uint8_t* codes, int64_t ld_codes,
+                              float* scales, hipStream_t stream) {
+  if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(ld_x) || !dim_ok(ld_codes)) return FP8Q_ERR_INVALID_ARG;
+  if (tile_axis != FP8Q_TILE_ROW && tile_axis != FP8Q_TILE_TOKEN_T) return FP8Q_ERR_INVALID_ARG;
+  if (scale_mode != FP8Q_SCALE_FREE && scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return FP8Q_OK;
+  if (!x_bf16 || !codes || !scales) return FP8Q_ERR_INVALID_ARG;
+  if (ld_x < cols) return FP8Q_ERR_SHAPE;
+  const int64_t code_row = tile_axis == FP8Q_TILE_ROW ? cols : rows;
+  if (ld_codes < code_row) return FP8Q_ERR_SHAPE;
+  const int64_t tiles = tile_axis == FP8Q_TILE_ROW ? rows * ((cols + 127) / 128) : cols * ((rows + 127) / 128);
+  if (tiles > kMaxDim || (tile_axis == FP8Q_TILE_TOKEN_T && (cols + 63) / 64 > 65535)) return FP8Q_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  const bool pow2 = scale_mode == FP8Q_SCALE_POW2;
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  if (tile_axis == FP8Q_TILE_ROW)
+    return launched(fp8q::launch_quant_rows(x, (int)rows, (int)cols, ld_x, pow2, codes, ld_codes, scales, stream));
+  return launched(fp8q::launch_quant_token_t(x, (int)rows, (int)cols, ld_x, pow2, codes, ld_codes, scales, stream));
+}
+
+fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w, int scale_mode,
+                                 uint8_t* codes, int64_t ld_codes, float* scales, hipStream_t stream) {
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(ld_w) || !dim_ok(ld_codes)) return FP8Q_ERR_INVALID_ARG;
+  if (scale_mode != FP8Q_SCALE_FREE && scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!w_bf16 || !codes || !scales) return FP8Q_ERR_INVALID_ARG;
+  if (ld_w < K || ld_codes < K) return FP8Q_ERR_SHAPE;
+  if (((N + 127) / 128) * ((K + 127) / 128) > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_quant_blocks(static_cast<const uint16_t*>(w_bf16), (int)N, (int)K, ld_w,
+                                            scale_mode == FP8Q_SCALE_POW2, codes, ld_codes, scales, stream));
+}
+
+namespace {
+fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t ld_c, int64_t N) {
+  if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
+  if (K % 128) return FP8Q_ERR_SHAPE;
+  if (!c) return FP8Q_ERR_INVALID_ARG;
+  if (ld_c < N) return FP8Q_ERR_SHAPE;
+  if (!aligned16(c)) return FP8Q_ERR_ALIGN;
+  return FP8Q_OK;
+}
+}  // namespace
+
+fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
+                      int64_t M, int64_t N, int64_t K, int out_dtype, void* c, int64_t ld_c,
+                      hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
+  if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
+  if (K > 0) {
+    if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
+  }
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_gemm(a, a_scales, w, w_scales, (int)M, (int)N, (int)K,
+                                    out_dtype == FP8Q_OUT_BF16, c, ld_c, stream));
+}
+
+fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
+                              int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N,
+                              int64_t K, int out_dtype, void* c, int64_t ld_c, hipStream_t stream) {
+  if (G < 0 || !dim_ok(rows_cap) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
+  if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
+  if (G == 0 || rows_cap == 0 || N == 0) return FP8Q_OK;
+  if (!offsets) return FP8Q_ERR_INVALID_ARG;
+  if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
+  const int64_t tiles = ((rows_cap + 255) / 256 + G) * ((N + 255) / 256);
+  if (tiles > kMaxDim || (int64_t)G * N * K > (int64_t(1) << 40)) return FP8Q_ERR_SHAPE;
+  if (K > 0) {
+    if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
+  }
+  if (!aligned16(offsets)) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_grouped_gemm(a, a_scales, offsets, (int)G, (int)rows_cap, w, w_scales, (int)N,
+                                            (int)K, out_dtype == FP8Q_OUT_BF16, c, ld_c, stream));
+}
+
+fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t, const float* x_scales,
+                       int64_t Nout, int64_t Kin, int64_t T, float* dw, int64_t ld_dw, hipStream_t stream) {
+  if (!dim_ok(Nout) || !dim_ok(Kin) || !dim_ok(T) || !dim_ok(ld_dw)) return FP8Q_ERR_INVALID_ARG;
+  if (Nout == 0 || Kin == 0) return FP8Q_OK;
+  if (fp8q_status st = check_gemm_common(T, FP8Q_OUT_F32, dw, ld_dw, Kin)) return st;
+  if (T > 0) {
+    if (!dy_t || !dy_scales || !x_t || !x_scales) return FP8Q_ERR_INVALID_ARG;
+    if (!aligned16(dy_t) || !aligned16(x_t) || !aligned16(dy_scales) || !aligned16(x_scales)) return FP8Q_ERR_ALIGN;
+  }
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_wgrad(dy_t, dy_scales, x_t, x_scales, (int)Nout, (int)Kin, (int)T, dw, ld_dw, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal declarations shared by the host entry points (fp8q_api.cpp) and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// Launchers validate nothing: fp8q_api.cpp has checked shapes, alignment and
+// the device before calling them.  Every size here is > 0 and < 2^31.
+hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
+                             uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
+hipError_t launch_quant_token_t(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
+                                uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
+hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
+                               uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                       const float* w_scales, int m, int n, int k, bool bf16_out, void* c,
+                       int64_t ldc, hipStream_t stream);
+hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets,
+                               int groups, int rows_cap, const uint8_t* w, const float* w_scales,
+                               int n, int k, bool bf16_out, void* c, int64_t ldc,
+                               hipStream_t stream);
+hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t,
+                        const float* x_scales, int nout, int kin, int t, float* dw, int64_t lddw,
+                        hipStream_t stream);
+
+}  // namespace fp8q

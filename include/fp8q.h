@@ -1,0 +1,152 @@
+/*
+ * fp8q -- fine-grained FP8 (E4M3) quantization and block-scaled GEMM for
+ * AMD Instinct MI355X (gfx950).  C ABI of libfp8q.so.
+ *
+ * What the library computes (pages cited by address and paragraph; they carry
+ * no titles or section numbers):
+ *
+ *  - why-be.co.kr wr_id=35533 ¶2: every GEMM operand is E4M3 (4-bit exponent,
+ *    3-bit mantissa).  The OCP variant is used: bias 7, largest finite 448,
+ *    NaN at S.1111.111, no infinities.
+ *  - jp-study.kr doc 258368 ¶1: scaling is online max-abs, per 1x128
+ *    activation tile and per 128x128 weight block.  A tile's scale is
+ *    s = RN32(amax / 448) and an element's code is E4M3_RNE(RN32(x / s))
+ *    (IEEE float32 division, then round-to-nearest-even to E4M3, saturating
+ *    at +-448, sign of zero kept).  An all-zero tile gets s = 0 and signed
+ *    zero codes.
+ *  - tmdrlife.com wr_id=13334 ¶4, gnrental.net wr_id=40936 ¶3: some
+ *    activations use power-of-two scales: s = the smallest 2^e with
+ *    amax / s <= 448, so x / s is exact.
+ *  - tmdrlife.com wr_id=13334 ¶3, gnrental.net wr_id=40936 ¶4, jp-study.kr
+ *    doc 258368 ¶3: the GEMM forms FP8 partial products over 128 elements of
+ *    K, then multiplies each partial by its activation and weight scales and
+ *    adds it into FP32 accumulators:
+ *        C[m,n] = sum_b a_scales[m,b] * w_scales[n/128,b] * sum_{k in b} A[m,k] W[n,k]
+ *  - jp-study.kr doc 258368 ¶3: the weight gradient (Wgrad) runs in FP8 too;
+ *    its reduction axis is the token axis, so both operands are quantized in
+ *    128-token x 1-feature tiles.
+ *
+ * Conventions for every call:
+ *  - Memory: all pointers are DEVICE pointers owned by the caller.  The
+ *    library allocates nothing, frees nothing and keeps no pointer after
+ *    the call returns.
+ *  - Execution: work is enqueued on `stream` (0 = the null stream) and the
+ *    call returns without synchronizing.  There is no global mutable state
+ *    beyond a per-device architecture check cached on first use, so calls
+ *    are re-entrant and thread-safe.
+ *  - Errors: argument errors are detected before anything is launched; the
+ *    outputs are then untouched.  A failed launch returns FP8Q_ERR_LAUNCH.
+ *    Faults inside kernels surface at the caller's next synchronization.
+ *    A current device that is not gfx950 gives FP8Q_ERR_DEVICE.
+ *  - Sizes: int64 values, each below 2^31.  Zero-sized outputs return
+ *    FP8Q_OK without launching.  Inputs must be finite.
+ *  - Alignment: every base pointer must be 16-byte aligned (FP8Q_ERR_ALIGN
+ *    otherwise).  Leading dimensions (in elements) only need to be at least
+ *    the row length; strides that break 16-byte row alignment are accepted
+ *    and take slower element-wise load/store paths.
+ *  - Aliasing between inputs and outputs is not allowed.
+ *  - BF16 data is passed as raw 16-bit patterns; codes are uint8 E4M3
+ *    patterns; scales are float32, always densely packed (no leading dim).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum fp8q_status {
+  FP8Q_OK = 0,
+  FP8Q_ERR_INVALID_ARG = 1, /* null pointer, negative size, unknown enum value */
+  FP8Q_ERR_SHAPE = 2,       /* leading dim below the row length, K not a multiple of 128, size >= 2^31 */
+  FP8Q_ERR_ALIGN = 3,       /* a base pointer is not 16-byte aligned */
+  FP8Q_ERR_LAUNCH = 4,      /* the HIP runtime rejected a kernel launch */
+  FP8Q_ERR_DEVICE = 5       /* no current device, or it is not gfx950 */
+} fp8q_status;
+
+enum { FP8Q_SCALE_FREE = 0, FP8Q_SCALE_POW2 = 1 };
+enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 };
+enum {
+  FP8Q_TILE_ROW = 0,    /* 1x128 tiles along cols: codes [rows, ld_codes], scales [rows, ceil(cols/128)] */
+  FP8Q_TILE_TOKEN_T = 1 /* 128x1 tiles along rows (the token axis), codes written transposed:
+                           codes [cols, ld_codes] with ld_codes >= rows, scales [cols, ceil(rows/128)] */
+};
+
+/* Quantize a BF16 activation x[rows, cols] (row stride ld_x elements) into
+ * E4M3 codes and float32 scales with online max-abs scaling per tile
+ * (jp-study.kr doc 258368 ¶1; power-of-two mode: tmdrlife.com wr_id=13334 ¶4).
+ * tile_axis: FP8Q_TILE_ROW (1x128 along the GEMM reduction axis, the last
+ * tile of a row may be ragged) or FP8Q_TILE_TOKEN_T (128x1 along rows; the
+ * output is feature-major so a token-axis GEMM reads it K-contiguous).
+ * scale_mode: FP8Q_SCALE_FREE or FP8Q_SCALE_POW2.  Codes outside the valid
+ * region of each output row are not written. */
+fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
+                              int tile_axis, int scale_mode,
+                              uint8_t* codes, int64_t ld_codes, float* scales,
+                              hipStream_t stream);
+
+/* Quantize a BF16 weight w[N, K] (row stride ld_w elements) per 128x128
+ * block (jp-study.kr doc 258368 ¶1).  codes [N, ld_codes];
+ * scales [ceil(N/128), ceil(K/128)] row-major.  Edge blocks may be ragged in
+ * both directions. */
+fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w,
+                                 int scale_mode,
+                                 uint8_t* codes, int64_t ld_codes, float* scales,
+                                 hipStream_t stream);
+
+/* Block-scaled GEMM C[M,N] = A . W^T (tmdrlife.com wr_id=13334 ¶3;
+ * jp-study.kr doc 258368 ¶3):
+ *   C[m,n] = sum_b a_scales[m,b] * w_scales[n/128,b] * sum_{k in block b} A[m,k] * W[n,k]
+ * a: codes [M, K] contiguous; a_scales [M, K/128]; w: codes [N, K]
+ * contiguous; w_scales [ceil(N/128), K/128].  K must be a multiple of 128
+ * (K = 0 writes zeros).  out_dtype FP8Q_OUT_F32 (c is float*) or
+ * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); row
+ * stride ld_c elements.  C is overwritten. */
+fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
+                      const uint8_t* w, const float* w_scales,
+                      int64_t M, int64_t N, int64_t K, int out_dtype,
+                      void* c, int64_t ld_c, hipStream_t stream);
+
+/* Grouped block-scaled GEMM for the MoE experts one device hosts
+ * (jp-study.kr doc 258368 ¶1-¶2: activations quantized before the expert
+ * dispatch; each device hosts several experts).  Rows
+ * [offsets[g], offsets[g+1]) of a use expert g's weights w[g]:
+ *   C[r,n] = sum_b a_scales[r,b] * w_scales[g, n/128, b] * sum_k A[r,k] * W[g,n,k]
+ * a: codes [rows_cap, K]; a_scales [rows_cap, K/128];
+ * offsets: DEVICE int32[G+1], non-decreasing, offsets[0] = 0,
+ *   offsets[G] <= rows_cap (precondition, not checked: it would need a
+ *   synchronization); empty groups are allowed;
+ * w: codes [G, N, K]; w_scales [G, ceil(N/128), K/128];
+ * c: [rows_cap, ld_c] in grouped (expert-sorted) row order; rows not
+ * covered by any group are not written. */
+fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales,
+                              const int32_t* offsets, int32_t G, int64_t rows_cap,
+                              const uint8_t* w, const float* w_scales,
+                              int64_t N, int64_t K, int out_dtype,
+                              void* c, int64_t ld_c, hipStream_t stream);
+
+/* FP8 weight gradient dW[Nout, Kin] = dY^T . X over T tokens
+ * (jp-study.kr doc 258368 ¶3):
+ *   dW[n,c] = sum_b dy_scales[n,b] * x_scales[c,b] * sum_{t in block b} dY[t,n] * X[t,c]
+ * Operands are FP8Q_TILE_TOKEN_T outputs with ld_codes = T: dy_t codes
+ * [Nout, T], dy_scales [Nout, T/128], x_t codes [Kin, T], x_scales
+ * [Kin, T/128].  T must be a multiple of 128 (T = 0 writes zeros).
+ * Output float32, row stride ld_dw elements, overwritten. */
+fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
+                       const uint8_t* x_t, const float* x_scales,
+                       int64_t Nout, int64_t Kin, int64_t T,
+                       float* dw, int64_t ld_dw, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* fp8q_status_string(fp8q_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,113 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status codes before
+touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_fp8_fp8q_amd as fp8q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+P16 = ctypes.c_void_p(4096)  # a non-null, 16-byte aligned address (never dereferenced)
+P8 = ctypes.c_void_p(4104)   # non-null, not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fp8q.LIB_PATH):
+        pytest.skip("libfp8q.so is not built")
+    return fp8q.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fp8q_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm", "fp8q_grouped_gemm", "fp8q_wgrad",
+              "fp8q_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(fp8q.SYMBOLS) == _declared()
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert fp8q.status_string(s)
+    assert fp8q.status_string(99) == "unknown status"
+
+
+def test_quantize_act_validation(lib):
+    q = lib.fp8q_quantize_act
+    # size 0 -> OK, nothing touched
+    assert q(None, 0, 5, 8, 0, 0, None, 16, None, None) == fp8q.OK
+    assert q(None, 5, 0, 8, 0, 0, None, 16, None, None) == fp8q.OK
+    assert q(None, -1, 5, 8, 0, 0, None, 16, None, None) == fp8q.ERR_INVALID_ARG
+    assert q(P16, 4, 8, 8, 2, 0, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG  # bad tile axis
+    assert q(P16, 4, 8, 8, 0, 7, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG  # bad scale mode
+    assert q(None, 4, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG
+    assert q(P16, 4, 16, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_SHAPE  # ld_x < cols
+    assert q(P16, 4, 8, 8, 0, 0, P16, 0, P16, None) == fp8q.ERR_SHAPE  # ld_codes < cols
+    assert q(P16, 40, 8, 8, 1, 0, P16, 16, P16, None) == fp8q.ERR_SHAPE  # token_t: ld_codes < rows
+    assert q(P8, 4, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_ALIGN
+    assert q(P16, 4, 8, 8, 0, 0, P8, 16, P16, None) == fp8q.ERR_ALIGN
+    assert q(P16, 4, 8, 8, 0, 0, P16, 16, P8, None) == fp8q.ERR_ALIGN
+    assert q(P16, 1 << 31, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG
+
+
+def test_quantize_weight_validation(lib):
+    q = lib.fp8q_quantize_weight
+    assert q(None, 0, 0, 0, 0, None, 0, None, None) == fp8q.OK
+    assert q(P16, 4, 8, 8, 3, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG
+    assert q(P16, 4, 16, 8, 0, P16, 16, P16, None) == fp8q.ERR_SHAPE
+    assert q(P16, 4, 8, 8, 0, P8, 16, P16, None) == fp8q.ERR_ALIGN
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8q_gemm
+    assert g(None, None, None, None, 0, 4, 128, 0, None, 4, None) == fp8q.OK
+    assert g(P16, P16, P16, P16, 4, 4, 100, 0, P16, 4, None) == fp8q.ERR_SHAPE  # K % 128
+    assert g(P16, P16, P16, P16, 4, 4, 128, 2, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(None, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(P16, P16, P16, P16, 4, 8, 128, 0, P16, 4, None) == fp8q.ERR_SHAPE  # ld_c < N
+    assert g(P16, P16, P16, P16, 4, 4, 128, 1, P8, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P8, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P16, P16, 4, 4, -128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+
+
+def test_grouped_and_wgrad_validation(lib):
+    gg = lib.fp8q_grouped_gemm
+    assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.OK  # no groups
+    assert gg(P16, P16, P16, -1, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, None, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, P16, 4, None) == fp8q.ERR_SHAPE
+    assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    wg = lib.fp8q_wgrad
+    assert wg(P16, P16, P16, P16, 0, 4, 128, P16, 4, None) == fp8q.OK
+    assert wg(P16, P16, P16, P16, 4, 4, 200, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, P16, P16, P16, 4, 8, 128, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, None, P16, P16, 4, 4, 128, P16, 4, None) == fp8q.ERR_INVALID_ARG
+
+
+def test_valid_calls_reach_the_device_check(lib):
+    """Well-formed arguments pass validation; without a gfx950 device the call
+    reports FP8Q_ERR_DEVICE and launches nothing."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_quantize_act(P16, 4, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_DEVICE
+    # leading dimensions need no alignment (unaligned strides take element-wise paths)
+    assert lib.fp8q_quantize_act(P16, 4, 7, 7, 0, 0, P16, 7, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, P16, 5, None) == fp8q.ERR_DEVICE

@@ -1,0 +1,221 @@
+"""GPU parity of the quantizers against the oracle: codes and scales must be
+bit-identical (jp-study.kr doc 258368 ¶1; tmdrlife.com wr_id=13334 ¶4).
+
+Covers the tiny-linear and dense-expert inputs in full, the quantize-only
+workload (16384 x 7168 activations in both scale modes, 7168 x 18432 weights)
+on sampled rows and block rows, ragged and strided shapes, special values,
+the exhaustive reachable (x, amax) space of several exponent bands, and
+run-to-run determinism.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_fp8q_amd as fp8q
+from oracle import quantize as Q
+import synth
+from tests.gpu_util import (assert_codes_equal, assert_scales_equal, dev_bf16, host, host_codes,
+                            need_gpu, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _check_rows(bits, mode, what, tile_axis="row"):
+    say(f"[quant] {what}: {tile_axis} {mode} shape={bits.shape}")
+    codes, scales = fp8q.quantize_act(dev_bf16(bits), tile_axis=tile_axis, scale_mode=mode)
+    if tile_axis == "row":
+        want_c, want_s = Q.quantize_rows(bits, mode)
+    else:
+        want_c, want_s = Q.quantize_token_t(bits, mode)
+    assert_codes_equal(host_codes(codes), want_c, what)
+    assert_scales_equal(host(scales), want_s, what)
+
+
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_tiny_linear_full(mode):
+    d = synth.tiny_linear()
+    _check_rows(d["a"], mode, "tiny A")
+    say(f"[quant] tiny W blocks {mode}")
+    c, s = fp8q.quantize_weight(dev_bf16(d["w"]), scale_mode=mode)
+    wc, ws = Q.quantize_blocks(d["w"], mode)
+    assert_codes_equal(host_codes(c), wc, "tiny W")
+    assert_scales_equal(host(s), ws, "tiny W")
+
+
+def _rand_bits(rng, shape, spread=8):
+    x = rng.standard_normal(shape) * np.exp2(rng.integers(-spread, spread + 1, shape))
+    return synth.bf16_rne(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 7), (2, 127), (5, 129), (17, 300), (64, 1024), (33, 640)])
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_ragged_rows(rows, cols, mode):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    _check_rows(_rand_bits(rng, (rows, cols)), mode, f"ragged {rows}x{cols}")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (128, 64), (300, 70), (129, 200), (512, 128), (256, 1000)])
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_ragged_token_axis(rows, cols, mode):
+    rng = np.random.default_rng(rows * 7 + cols)
+    _check_rows(_rand_bits(rng, (rows, cols)), mode, f"token_t {rows}x{cols}", tile_axis="token_t")
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (128, 128), (200, 300), (257, 129), (384, 640)])
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_ragged_blocks(n, k, mode):
+    rng = np.random.default_rng(n * 13 + k)
+    bits = _rand_bits(rng, (n, k))
+    say(f"[quant] blocks {n}x{k} {mode}")
+    c, s = fp8q.quantize_weight(dev_bf16(bits), scale_mode=mode)
+    wc, ws = Q.quantize_blocks(bits, mode)
+    assert_codes_equal(host_codes(c), wc, "blocks")
+    assert_scales_equal(host(s), ws, "blocks")
+
+
+def test_strided_input_rows_and_blocks():
+    rng = np.random.default_rng(21)
+    full = _rand_bits(rng, (40, 320))
+    xd = dev_bf16(full)[:, :300]  # row stride 320 elements
+    say("[quant] strided rows 40x300 (ld 320)")
+    c, s = fp8q.quantize_act(xd, "row", "free")
+    wc, ws = Q.quantize_rows(np.ascontiguousarray(full[:, :300]), "free")
+    assert_codes_equal(host_codes(c), wc, "strided rows")
+    assert_scales_equal(host(s), ws, "strided rows")
+    c, s = fp8q.quantize_weight(xd, "pow2")
+    wc, ws = Q.quantize_blocks(np.ascontiguousarray(full[:, :300]), "pow2")
+    assert_codes_equal(host_codes(c), wc, "strided blocks")
+    assert_scales_equal(host(s), ws, "strided blocks")
+
+
+def _special_rows():
+    """Tiles of zeros, negative zeros, BF16 subnormals, tiny and huge values."""
+    rows = []
+    z = np.zeros(256, np.uint16)
+    rows.append(z.copy())
+    nz = z.copy()
+    nz[::3] = 0x8000  # -0
+    rows.append(nz)
+    sub = np.arange(256, dtype=np.uint16) % 128  # BF16 subnormals (and zeros)
+    sub[1::2] |= 0x8000
+    rows.append(sub)
+    for ebits in (1, 2, 30, 36, 37, 38, 200, 254):  # around the normal min, the IEEE/Markstein switch, the max
+        r = np.random.default_rng(ebits).integers(0, (ebits << 7) | 0x7F, 256).astype(np.uint16)
+        r[0] = (ebits << 7) | 0x7F
+        r[130] = (ebits << 7) | 0x60
+        r[1::5] |= 0x8000
+        rows.append(r)
+    big = np.full(256, 0x7F7F, np.uint16)  # largest finite BF16
+    big[1::2] = 0xFF7F
+    rows.append(big)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_special_values(mode):
+    bits = _special_rows()
+    _check_rows(bits, mode, "special rows")
+    _check_rows(np.ascontiguousarray(bits.T), mode, "special token_t", tile_axis="token_t")
+    say(f"[quant] special blocks {mode}")
+    c, s = fp8q.quantize_weight(dev_bf16(bits), scale_mode=mode)
+    wc, ws = Q.quantize_blocks(bits, mode)
+    assert_codes_equal(host_codes(c), wc, "special blocks")
+    assert_scales_equal(host(s), ws, "special blocks")
+
+
+def reachable_band(ebits, seed):
+    """Every (x, amax) pair with amax in one BF16 binade and |x| <= amax.
+
+    Row i of the result is a 128-element tile whose element 0 is the amax
+    (random sign) and whose other elements are x values (random signs).  For
+    each of the 128 amax significands of the binade, all BF16 magnitudes from
+    0 up to amax are covered.
+    """
+    rng = np.random.default_rng(seed)
+    tiles = []
+    for mant in range(128):
+        ab = (ebits << 7) | mant
+        if ab == 0:
+            continue
+        xs = np.arange(0, ab + 1, dtype=np.uint32).astype(np.uint16)
+        xs |= (rng.integers(0, 2, xs.size) << 15).astype(np.uint16)
+        pad = (-xs.size) % 127
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        head = np.full((xs.shape[0], 1), ab, np.uint16) | (rng.integers(0, 2, (xs.shape[0], 1)) << 15).astype(np.uint16)
+        tiles.append(np.concatenate([head, xs], axis=1))
+    return np.concatenate(tiles)
+
+
+@pytest.mark.parametrize("ebits", [0, 1, 36, 37, 100, 127, 160, 254])
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_exhaustive_reachable_space(ebits, mode):
+    bits = reachable_band(ebits, seed=ebits)
+    _check_rows(bits, mode, f"reachable band e={ebits}")
+
+
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_quantize_only_activations_sampled_rows(mode):
+    act = synth.quant_only_act()
+    say(f"[quant] quantize-only activations 16384x7168 {mode}")
+    codes, scales = fp8q.quantize_act(dev_bf16(act), "row", mode)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(act.shape[0] - 64, act.shape[0]),
+                                     rng.integers(0, act.shape[0], 192)]))
+    wc, ws = Q.quantize_rows(act[rows], mode)
+    idx = torch.from_numpy(rows).to(codes.device)
+    assert_codes_equal(host_codes(codes.index_select(0, idx)), wc, "act rows")
+    assert_scales_equal(host(scales.index_select(0, idx)), ws, "act rows")
+
+
+def test_quantize_only_weights_sampled_block_rows():
+    w = synth.quant_only_weight()
+    say("[quant] quantize-only weights 7168x18432")
+    codes, scales = fp8q.quantize_weight(dev_bf16(w), "free")
+    sc = host(scales)
+    for bi in (0, 27, 55):
+        lo, hi = bi * 128, (bi + 1) * 128
+        wc, ws = Q.quantize_blocks(w[lo:hi], "free")
+        assert_codes_equal(host_codes(codes[lo:hi]), wc, f"weight block row {bi}")
+        assert_scales_equal(sc[bi:bi + 1], ws, f"weight block row {bi}")
+
+
+def test_dense_up_projection_inputs_full():
+    d = synth.dense_up()
+    _check_rows(d["a"], "free", "dense A 4096x7168")
+    say("[quant] dense W 4096x7168 blocks")
+    c, s = fp8q.quantize_weight(dev_bf16(d["w"]), "free")
+    wc, ws = Q.quantize_blocks(d["w"], "free")
+    assert_codes_equal(host_codes(c), wc, "dense W")
+    assert_scales_equal(host(s), ws, "dense W")
+
+
+def test_wgrad_inputs_token_axis_sampled():
+    d = synth.wgrad(tokens=4096)
+    _check_rows(d["dy"], "free", "wgrad dY 4096x2048", tile_axis="token_t")
+    _check_rows(d["x"][:, :1024], "pow2", "wgrad X 4096x1024", tile_axis="token_t")
+
+
+def test_quantize_then_gather_equals_gather_then_quantize():
+    """jp-study.kr doc 258368 ¶1: activations are quantized before dispatch."""
+    d = synth.moe_grouped(tokens=1024, with_weights=False)
+    x = dev_bf16(d["x"])
+    gather = torch.from_numpy(d["gather"]).to(x.device)
+    say("[quant] quantize-then-gather")
+    c1, s1 = fp8q.quantize_act(x, "row", "free")
+    c2, s2 = fp8q.quantize_act(x.index_select(0, gather).contiguous(), "row", "free")
+    assert torch.equal(c1.index_select(0, gather), c2) and torch.equal(s1.index_select(0, gather), s2)
+
+
+def test_deterministic():
+    d = synth.tiny_linear()
+    x = dev_bf16(d["a"])
+    say("[quant] determinism")
+    a = fp8q.quantize_act(x, "row", "free")
+    b = fp8q.quantize_act(x, "row", "free")
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
