@@ -23,9 +23,12 @@ SOURCES = ["quant.hip", "gemm.hip", "fp8q_api.cpp"]
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly (the quotient correction and the scale fold depend on it).
 # -packed-fp32-ops: no packed FP32 VALU instructions are generated.
+# -amdgpu-mfma-vgpr-form: MFMA results land in VGPRs, where the FP32 scale
+# fold reads them, instead of AGPRs that would need a copy per element.
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -88,6 +88,9 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
 }
 
 namespace {
+// GEMM kernels address an operand with 32-bit byte offsets.
+constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
+
 fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t ld_c, int64_t N) {
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
   if (K % 128) return FP8Q_ERR_SHAPE;
@@ -105,6 +108,7 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
+  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
   if (K > 0) {
     if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
@@ -123,7 +127,8 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int
   if (!offsets) return FP8Q_ERR_INVALID_ARG;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
   const int64_t tiles = ((rows_cap + 255) / 256 + G) * ((N + 255) / 256);
-  if (tiles > kMaxDim || (int64_t)G * N * K > (int64_t(1) << 40)) return FP8Q_ERR_SHAPE;
+  if (tiles > kMaxDim || rows_cap * K >= kMaxOperandBytes || int64_t(G) * N * K >= kMaxOperandBytes)
+    return FP8Q_ERR_SHAPE;
   if (K > 0) {
     if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
@@ -139,6 +144,7 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
   if (!dim_ok(Nout) || !dim_ok(Kin) || !dim_ok(T) || !dim_ok(ld_dw)) return FP8Q_ERR_INVALID_ARG;
   if (Nout == 0 || Kin == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(T, FP8Q_OUT_F32, dw, ld_dw, Kin)) return st;
+  if (Nout * T >= kMaxOperandBytes || Kin * T >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
   if (T > 0) {
     if (!dy_t || !dy_scales || !x_t || !x_scales) return FP8Q_ERR_INVALID_ARG;
     if (!aligned16(dy_t) || !aligned16(x_t) || !aligned16(dy_scales) || !aligned16(x_scales)) return FP8Q_ERR_ALIGN;

@@ -33,9 +33,9 @@
 // a row XOR-swizzled so the fragment reads (ds_read_b128, 16 rows at the
 // same chunk) hit distinct banks.  Lane group g (lanes 16g..16g+15) reads
 // bytes 32g..32g+31 of its row; the k order inside a block only has to be
-// the same for both operands.  Two LDS stages: the next K block streams in
-// while the current one is multiplied; one barrier per K block.  The
-// per-row scales of the K block ride along in the same stage.
+// the same for both operands.  Three LDS stages: K block kb+2 streams in
+// while kb is multiplied; one barrier per K block.  The per-row scales of
+// the K block ride along in the same stage.
 #include "fp8q_internal.h"
 
 namespace fp8q {
@@ -55,6 +55,9 @@ constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [12
 constexpr int kStageBytes = kScaleOff + (BM + BN) * 4;           // 49.5 KiB
 
 enum Mode { kDense = 0, kGrouped = 1, kWgrad = 2 };
+
+// Buffer resource word 3 for raw (untyped, unswizzled) buffer access.
+constexpr int kRsrcFlags = 0x00020000;
 
 struct GemmArgs {
   const uint8_t* a;       // codes [rows, k]
@@ -146,57 +149,80 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
   }
 }
 
+// One K block of the main loop.  `cur` (the stage multiplied now) and
+// `refill` (the stage the loads of block kb+2 go to) are distinct LDS
+// buffers; __restrict__ tells the compiler so, which lets it keep the refill
+// loads in flight across the LDS reads of `cur` instead of waiting for them.
+template <class Issue, class Compute>
+__device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restrict__ cur,
+                                         uint8_t* __restrict__ refill, Issue& issue, Compute& compute) {
+  asm volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
+  // Past the last block the refill re-reads the last block (in bounds) into
+  // a stage that is never read again: the issue stays unconditional, which
+  // keeps the compiler's tracking of the loads in flight exact.
+  issue(min(kb + 2, nkb - 1), refill);
+  compute(cur);
+}
+
 template <int MODE, bool BF16OUT>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
 
   Tile t;
   if (!decode_tile<MODE>(g, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses
   const int wm = wave & 1, wn = wave >> 1;
   const int K = g.k, N = g.n;
   const int nkb = K / BK;
 
   // ---- global->LDS assignment: one wave instruction moves 8 rows x 128 B.
-  // Wave w moves A rows 32w..32w+31 and W rows 64w..64w+63.
-  int64_t a_off[4], w_off[8];
+  // Wave w moves A rows 32w..32w+31 and W rows 64w..64w+63.  Loads are
+  // buffer loads with an LDS destination: a per-lane 32-bit byte offset
+  // (VGPR, fixed for the whole K loop), the K-block offset in an SGPR, the
+  // LDS address in M0, so issuing costs no VALU work.  Byte offsets fit in
+  // 32 bits (the host rejects operands of 2 GiB or more).
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, 0, 0x7FFFFFFF, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)t.w, 0, 0x7FFFFFFF, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.sa, 0, 0x7FFFFFFF, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t sw_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)t.sw, 0, 0x7FFFFFFF, kRsrcFlags);
+  uint32_t a_off[4], w_off[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wave * 4 + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);
-    a_off[i] = (int64_t)min(t.m0 + row, t.mend - 1) * K + 16 * chunk;
+    a_off[i] = (uint32_t)min(t.m0 + row, t.mend - 1) * (uint32_t)K + 16u * chunk;
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);
-    w_off[i] = (int64_t)min(t.n0 + row, N - 1) * K + 16 * chunk;
+    w_off[i] = (uint32_t)min(t.n0 + row, N - 1) * (uint32_t)K + 16u * chunk;
   }
-  // scales of the K block: waves 0-1 bring the A scales of rows 64w..64w+63,
-  // every wave the W scale of columns 64w..64w+63 (one value per column, so
-  // all modes share the LDS layout)
-  const float* sa_src = g.sa + (int64_t)min(t.m0 + (wave & 1) * 64 + lane, t.mend - 1) * nkb;
+  // scales of the K block: wave w brings the A scales of rows 64(w&1)..+63
+  // (waves 2-3 repeat waves 0-1's load, so every wave issues the same number
+  // of loads per stage) and the W scale of columns 64w..64w+63 (one value per
+  // column, so all modes share the LDS layout)
+  const uint32_t sa_off = (uint32_t)min(t.m0 + (wave & 1) * 64 + lane, t.mend - 1) * (uint32_t)nkb * 4u;
   const int wcol = min(t.n0 + wave * 64 + lane, N - 1);
-  const float* sw_src = t.sw + (int64_t)((MODE == kWgrad) ? wcol : (wcol >> 7)) * nkb;
+  const uint32_t sw_off = (uint32_t)((MODE == kWgrad) ? wcol : (wcol >> 7)) * (uint32_t)nkb * 4u;
 
   auto issue = [&](int kb, uint8_t* st) {
-    const int64_t kofs = (int64_t)kb * BK;
+    const uint32_t kofs = (uint32_t)kb * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(g.a + a_off[i] + kofs, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, a_off[i], kofs, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_global_load_lds(t.w + w_off[i] + kofs, (lds_void_ptr)(st + kATileBytes + (wave * 8 + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + kATileBytes + (wave * 8 + i) * 1024), 16, w_off[i], kofs, 0, 0);
     }
-    if (wave < 2) {
-      __builtin_amdgcn_global_load_lds(sa_src + kb, (lds_void_ptr)(st + kScaleOff + wave * 256), 4, 0, 0);
-    }
-    __builtin_amdgcn_global_load_lds(sw_src + kb, (lds_void_ptr)(st + kScaleOff + BM * 4 + wave * 256), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sa_rsrc, (lds_void_ptr)(st + kScaleOff + (wave & 1) * 256), 4, sa_off, (uint32_t)kb * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rsrc, (lds_void_ptr)(st + kScaleOff + BM * 4 + wave * 256), 4, sw_off, (uint32_t)kb * 4u, 0, 0);
   };
 
   v4f acc[4][8];
@@ -209,77 +235,137 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   const int r16 = lane & 15;
   const int c0 = 2 * (lane >> 4);
 
+  // One K block: 8 W fragments (j) x 4 M fragments (f) x 4 K steps of 32 (q)
+  // = 128 MFMAs per wave.  Explicit software pipeline, in program order:
+  //   - all LDS reads of the block's A fragments and of W fragments 0 and 1
+  //     are issued first; A fragments are widened just in time, q-part by
+  //     q-part, inside W fragment 0, so the first MFMAs wait for 20
+  //     conversions rather than 80;
+  //   - W fragment j+1 is widened to BF16 during j, q-part by q-part, each
+  //     into the slot whose MFMAs have all been issued; each half of its
+  //     E4M3 bytes, once widened, is refilled from LDS with fragment j+2's,
+  //     three MFMA groups ahead of use;
+  //   - the four partial chains (f) are interleaved, so an MFMA never waits
+  //     for the one it accumulates onto;
+  //   - the fold of fragment j's partial for M fragment f is placed right
+  //     before the first MFMA of fragment j+1 that overwrites it, 4 MFMAs
+  //     after its last one.
+  // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
   auto compute = [&](const uint8_t* st) {
     if (!active) return;
     const float* S = reinterpret_cast<const float*>(st + kScaleOff);
-    // A fragments of the 4 M sub-tiles, widened to BF16: [f][q], q = 8-byte step
-    v8bf af[4][4];
+    const uint8_t* Ws = st + kATileBytes;
+    const int wrow0 = wn * 128 + r16;
+    const int wsw = swz(wrow0);  // same swizzle for rows wrow0 + 16j
+    auto read_w_lo = [&](int j, v4i& lo) {
+      lo = *reinterpret_cast<const v4i*>(Ws + (wrow0 + j * 16) * 128 + 16 * (c0 ^ wsw));
+    };
+    auto read_w_hi = [&](int j, v4i& hi) {
+      hi = *reinterpret_cast<const v4i*>(Ws + (wrow0 + j * 16) * 128 + 16 * ((c0 + 1) ^ wsw));
+    };
+    auto part = [](const v4i& lo, const v4i& hi, int q) {
+      const v4i& r = q < 2 ? lo : hi;
+      return e4m3x8_to_bf16(r[(q & 1) * 2], r[(q & 1) * 2 + 1]);
+    };
+    v4i w0lo, w0hi, wlo, whi;  // E4M3 bytes of W fragment 0 and of the next one
+    read_w_lo(0, w0lo);
+    read_w_hi(0, w0hi);
+    v4i alo[4], ahi[4];
     float sa[4];
+    const int arow0 = wm * 64 + r16;
+    const int asw = swz(arow0);  // same swizzle for rows arow0 + 16f
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const int row = wm * 64 + f * 16 + r16;
-      const int s = swz(row);
-      const v4i lo = *reinterpret_cast<const v4i*>(st + row * 128 + 16 * (c0 ^ s));
-      const v4i hi = *reinterpret_cast<const v4i*>(st + row * 128 + 16 * ((c0 + 1) ^ s));
-      af[f][0] = e4m3x8_to_bf16(lo[0], lo[1]);
-      af[f][1] = e4m3x8_to_bf16(lo[2], lo[3]);
-      af[f][2] = e4m3x8_to_bf16(hi[0], hi[1]);
-      af[f][3] = e4m3x8_to_bf16(hi[2], hi[3]);
-      sa[f] = S[row];
+      const uint8_t* base = st + (arow0 + f * 16) * 128;
+      alo[f] = *reinterpret_cast<const v4i*>(base + 16 * (c0 ^ asw));
+      ahi[f] = *reinterpret_cast<const v4i*>(base + 16 * ((c0 + 1) ^ asw));
     }
+    read_w_lo(1, wlo);
+    read_w_hi(1, whi);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
     float sc[4];
     if constexpr (MODE != kWgrad) {
       const float swv = S[BM + wn * 128];
 #pragma unroll
       for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
     }
-    const uint8_t* Ws = st + kATileBytes;
+
+    v8bf af[4][4];  // A fragments widened to BF16: [f][q]
+    v8bf bf[4];     // the current W fragment widened to BF16: [q]
+    v4f p[4];
+    auto fold = [&](int j, int f) {
+      if constexpr (MODE == kWgrad) {
+        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * 128 + j * 16 + 4 * (lane >> 4));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sc[f], acc[f][j][v]);
+      }
+    };
+
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = wn * 128 + j * 16 + r16;
-      const int s = swz(row);
-      const v4i lo = *reinterpret_cast<const v4i*>(Ws + row * 128 + 16 * (c0 ^ s));
-      const v4i hi = *reinterpret_cast<const v4i*>(Ws + row * 128 + 16 * ((c0 + 1) ^ s));
-      v8bf bf[4];
-      bf[0] = e4m3x8_to_bf16(lo[0], lo[1]);
-      bf[1] = e4m3x8_to_bf16(lo[2], lo[3]);
-      bf[2] = e4m3x8_to_bf16(hi[0], hi[1]);
-      bf[3] = e4m3x8_to_bf16(hi[2], hi[3]);
-      v4f swj;
-      if constexpr (MODE == kWgrad) {
-        swj = *reinterpret_cast<const v4f*>(S + BM + wn * 128 + j * 16 + 4 * (lane >> 4));
-      }
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        v4f p = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 4; ++q) {
+        if (j == 0) {  // widen W fragment 0 and the A fragments just in time
+          bf[q] = part(w0lo, w0hi, q);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[q], af[f][q], p, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float scale;
-          if constexpr (MODE == kWgrad) {
-            scale = sa[f] * swj[v];
-          } else {
-            scale = sc[f];
-          }
-          acc[f][j][v] = __builtin_fmaf(p[v], scale, acc[f][j][v]);
+          for (int f = 0; f < 4; ++f) af[f][q] = part(alo[f], ahi[f], q);
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if (q == 0 && j > 0) fold(j - 1, f);
+          p[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[q], af[f][q],
+                                                          q == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : p[f], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // slot q is no longer needed by fragment j: widen fragment j+1's part
+        if (j < 7) bf[q] = part(wlo, whi, q);
+        // a consumed half of fragment j+1's bytes is refilled with fragment
+        // j+2's right away: three MFMA groups before it is needed
+        if (q == 1 && j < 6) read_w_lo(j + 2, wlo);
+        if (q == 3 && j < 6) read_w_hi(j + 2, whi);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+#pragma unroll
+    for (int f = 0; f < 4; ++f) fold(7, f);
   };
 
-  if (nkb > 0) issue(0, stage0);
-  for (int kb = 0; kb < nkb; kb += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 1 < nkb) issue(kb + 1, stage1);
-    compute(stage0);
-    if (kb + 1 >= nkb) break;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kb + 2 < nkb) issue(kb + 2, stage0);
-    compute(stage1);
+  // Three LDS stages: block kb+2 streams in while kb is multiplied.  Each
+  // wave issues 14 loads per stage and loads complete in order, so at the
+  // top of block kb, vmcnt <= 14 means block kb has landed (block kb+1 is
+  // still in flight); the barrier then makes every wave's part visible and
+  // guarantees the stage being refilled (that of kb-1) is no longer read.
+  if (nkb > 0) {
+    issue(0, stage0);
+    issue(min(1, nkb - 1), stage1);
   }
+  // The barrier (in run_step) is a bare s_barrier: __syncthreads() would
+  // add a release fence, i.e. vmcnt(0), and wait for block kb+1 too.  It is sufficient
+  // here: each wave's loads of block kb have landed in LDS (vmcnt), and every
+  // LDS read of the stage being refilled was consumed by MFMAs or folds of
+  // the previous block before its wave reached the barrier.  The asm memory
+  // clobber keeps the compiler from moving LDS accesses across it.
+  auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
+    run_step(kb, nkb, cur, refill, issue, compute);
+  };
+  // Main loop without early exits (each stage keeps a fixed buffer, so the
+  // compiler can tell the LDS reads of one stage from the loads into another),
+  // then the remaining one or two blocks.
+  int kb = 0;
+  for (; kb + 3 <= nkb; kb += 3) {
+    step(kb, stage0, stage2);
+    step(kb + 1, stage1, stage0);
+    step(kb + 2, stage2, stage1);
+  }
+  if (kb < nkb) step(kb, stage0, stage2);
+  if (kb + 1 < nkb) step(kb + 1, stage1, stage0);
+  // no load may still be writing this workgroup's LDS when its waves exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds C[m][n..n+3]
 #pragma unroll
