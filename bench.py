@@ -9,9 +9,9 @@ resident before the timed region starts.
 
 Prints one JSON line:
   value      = whole-step throughput, 2*M*N*K / step time (TFLOP/s)
-  kernels    = per-kernel average durations from HIP events recorded on the
-               launch stream around each kernel in every timed step, with GB/s
-               or TFLOP/s and the fraction of the MI355X roofline
+  kernels    = per-kernel average durations from HIP events on the launch
+               stream around --steps back-to-back launches of that kernel,
+               with GB/s or TFLOP/s and the fraction of the MI355X roofline
   roofline   = the dominant kernel (the GEMM) against the dense FP8 MFMA peak
   cpu_baseline = the oracle timed on the host on a bounded sample
 
@@ -50,7 +50,28 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 256 MiB device-to-device copy (torch) --steps times; used to "
+                        "scale the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run")
     return p.parse_args()
+
+
+def copy_calibration(steps):
+    """A plain copy of known size: 256 MiB read + 256 MiB written per launch."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us": round(us, 2),
+                      "GB/s": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline():
@@ -77,8 +98,65 @@ def cpu_baseline():
                       f"rate = GEMM FLOPs / total"}
 
 
+def quantize_only_rates(torch, fp8q, lib, stream, reps):
+    """Quantizer bandwidth at the quantize-only sizes: activations 16384 x 7168
+    (standard Student-t(3)) in free and power-of-two modes, weights 7168 x 18432
+    (~N(0, 0.02)).  HIP events around `reps` launches alternating over two
+    input/output sets (each set is larger than the Infinity Cache)."""
+    import synth
+    dev = torch.device("cuda:0")
+    out = {}
+    act = synth.quant_only_act()
+    rows, cols = act.shape
+    xs = [torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).to(dev)]
+    xs.append(xs[0].clone())
+    cs = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(2)]
+    ss = torch.empty((rows, cols // 128), dtype=torch.float32, device=dev)
+    abytes = rows * cols * 3 + rows * (cols // 128) * 4
+    for mode_name, mode in (("free", fp8q.SCALE_FREE), ("pow2", fp8q.SCALE_POW2)):
+        def fn(i):
+            return lib.fp8q_quantize_act(xs[i & 1].data_ptr(), rows, cols, cols, fp8q.TILE_ROW, mode,
+                                         cs[i & 1].data_ptr(), cols, ss.data_ptr(), stream.cuda_stream)
+        us = _event_us(torch, stream, fn, reps)
+        out[f"act_16384x7168_{mode_name}"] = {"us": round(us, 2), "GB/s": round(abytes / us / 1e3, 1),
+                                              "frac_hbm": round(abytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                              "bytes": abytes}
+    del xs, cs, ss
+    wt = synth.quant_only_weight()
+    n, k = wt.shape
+    ws = [torch.from_numpy(wt.view(np.int16)).view(torch.bfloat16).to(dev)]
+    ws.append(ws[0].clone())
+    cs = [torch.empty((n, k), dtype=torch.uint8, device=dev) for _ in range(2)]
+    ss = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+    wbytes = n * k * 3 + (n // 128) * (k // 128) * 4
+
+    def fw(i):
+        return lib.fp8q_quantize_weight(ws[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, cs[i & 1].data_ptr(),
+                                        k, ss.data_ptr(), stream.cuda_stream)
+    us = _event_us(torch, stream, fw, reps)
+    out["weight_7168x18432"] = {"us": round(us, 2), "GB/s": round(wbytes / us / 1e3, 1),
+                                "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wbytes}
+    return out
+
+
+def _event_us(torch, stream, fn, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn(0)
+    fn(1)
+    e0.record(stream)
+    for i in range(reps):
+        if fn(i) != 0:
+            raise RuntimeError("fp8q call failed")
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -104,21 +182,20 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        st = lib.fp8q_quantize_act(a.data_ptr(), M, K, K, fp8q.TILE_ROW, fp8q.SCALE_FREE,
-                                   a_codes.data_ptr(), K, a_scales.data_ptr(), sp)
-        if ev is not None:
-            ev[1].record(stream)
-        st |= lib.fp8q_quantize_weight(w.data_ptr(), N, K, K, fp8q.SCALE_FREE, w_codes.data_ptr(), K,
-                                       w_scales.data_ptr(), sp)
-        if ev is not None:
-            ev[2].record(stream)
-        st |= lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
-                            M, N, K, fp8q.OUT_BF16, c.data_ptr(), N, sp)
-        if ev is not None:
-            ev[3].record(stream)
+    def q_act():
+        return lib.fp8q_quantize_act(a.data_ptr(), M, K, K, fp8q.TILE_ROW, fp8q.SCALE_FREE,
+                                     a_codes.data_ptr(), K, a_scales.data_ptr(), sp)
+
+    def q_wgt():
+        return lib.fp8q_quantize_weight(w.data_ptr(), N, K, K, fp8q.SCALE_FREE, w_codes.data_ptr(), K,
+                                        w_scales.data_ptr(), sp)
+
+    def gemm():
+        return lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
+                             M, N, K, fp8q.OUT_BF16, c.data_ptr(), N, sp)
+
+    def step():
+        st = q_act() | q_wgt() | gemm()
         if st != fp8q.OK:
             raise RuntimeError(f"fp8q call failed with status {st}")
 
@@ -126,17 +203,50 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # timed region: K whole steps, nothing else on the stream
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
     ms_step = (t1 - t0) * 1e3 / args.steps
-    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events])  # ms
-    qa_us, qw_us, gemm_us = (dur.mean(axis=0) * 1e3).tolist()
+
+    # per-kernel durations: HIP events on the launch stream around --steps
+    # back-to-back launches of one kernel (an event record is a queue barrier
+    # packet, so one pair per run keeps it out of the average).  The
+    # quantizers rotate over ROT copies of their input and output (more than
+    # the 256 MB Infinity Cache), so each launch streams from HBM as in the
+    # step; the GEMM re-reads its 58 MB of codes, which in the step were just
+    # written by the quantizers.
+    ROT = 5
+    a_rot = [a] + [a.clone() for _ in range(ROT - 1)]
+    w_rot = [w] + [w.clone() for _ in range(ROT - 1)]
+    ac_rot = [torch.empty_like(a_codes) for _ in range(ROT)]
+    wc_rot = [torch.empty_like(w_codes) for _ in range(ROT)]
+
+    def q_act_i(i):
+        return lib.fp8q_quantize_act(a_rot[i % ROT].data_ptr(), M, K, K, fp8q.TILE_ROW, fp8q.SCALE_FREE,
+                                     ac_rot[i % ROT].data_ptr(), K, a_scales.data_ptr(), sp)
+
+    def q_wgt_i(i):
+        return lib.fp8q_quantize_weight(w_rot[i % ROT].data_ptr(), N, K, K, fp8q.SCALE_FREE,
+                                        wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
+
+    def kernel_us(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(ROT):
+            fn(i)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    qa_us = kernel_us(q_act_i)
+    qw_us = kernel_us(q_wgt_i)
+    gemm_us = kernel_us(lambda i: gemm())
+    quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     qa_gbs = ACT_BYTES / (qa_us * 1e-6) / 1e9
     qw_gbs = WGT_BYTES / (qw_us * 1e-6) / 1e9
     gemm_tflops = GEMM_FLOP / (gemm_us * 1e-6) / 1e12
@@ -166,6 +276,7 @@ def main():
             "gemm_block_scaled": {"us": round(gemm_us, 2), "TFLOP/s": round(gemm_tflops, 1),
                                   "frac_fp8_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
         },
+        "quantize_only": quant_only,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": GEMM_TRAFFIC_BYTES},

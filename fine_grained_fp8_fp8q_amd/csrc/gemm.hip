@@ -20,8 +20,9 @@
 // their float32 result is the block's partial, folded with one v_fma_f32 per
 // element (the pages' "promotion"), while the MFMAs of the next fragment run.
 //
-// Workgroup tile 128 x 256 x 128, 4 waves (2 along M x 2 along N, one per
-// SIMD so each wave may hold up to 512 registers), wave tile 64 x 128.  The MFMA computes the transposed tile (W rows as its A operand,
+// Workgroup tile 256 x 256 x 128, 8 waves (4 along M x 2 along N: two per
+// SIMD, so one wave's LDS waits and conversions overlap the other's MFMAs),
+// wave tile 64 x 128 in at most 256 registers.  The MFMA computes the transposed tile (W rows as its A operand,
 // A rows as its B operand), so each lane owns one output row m and four
 // consecutive columns n: with 1x128 activation scales and 128x128 weight
 // blocks the fold scale a[m] * w[n/128] is one value per lane and per 16-row
@@ -33,9 +34,9 @@
 // a row XOR-swizzled so the fragment reads (ds_read_b128, 16 rows at the
 // same chunk) hit distinct banks.  Lane group g (lanes 16g..16g+15) reads
 // bytes 32g..32g+31 of its row; the k order inside a block only has to be
-// the same for both operands.  Three LDS stages: K block kb+2 streams in
-// while kb is multiplied; one barrier per K block.  The per-row scales of
-// the K block ride along in the same stage.
+// the same for both operands.  Two LDS stages (66 KiB each): K block kb+1
+// streams in while kb is multiplied; one barrier per K block.  The per-row
+// scales of the K block ride along in the same stage.
 #include "fp8q_internal.h"
 
 namespace fp8q {
@@ -47,8 +48,8 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-constexpr int BM = 128, BN = 256, BK = 128;
-constexpr int kThreads = 256;
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kThreads = 512;
 constexpr int kATileBytes = BM * BK;                             // 16 KiB
 constexpr int kWTileBytes = BN * BK;                             // 32 KiB
 constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [128], W scales [256]
@@ -150,17 +151,22 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
 }
 
 // One K block of the main loop.  `cur` (the stage multiplied now) and
-// `refill` (the stage the loads of block kb+2 go to) are distinct LDS
+// `refill` (the stage the loads of block kb+1 go to) are distinct LDS
 // buffers; __restrict__ tells the compiler so, which lets it keep the refill
 // loads in flight across the LDS reads of `cur` instead of waiting for them.
+// The barrier is a bare s_barrier after an explicit vmcnt(0): every wave's
+// loads of block kb have landed, and every LDS read of the stage being
+// refilled was consumed before its wave got here; __syncthreads() would add
+// nothing but a fence.  The asm memory clobber keeps the compiler from
+// moving LDS accesses across it.  Past the last block the refill re-reads
+// the last block (in bounds) into a stage that is never read again, so the
+// issue stays unconditional and the compiler's tracking of the loads in
+// flight stays exact.
 template <class Issue, class Compute>
 __device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restrict__ cur,
                                          uint8_t* __restrict__ refill, Issue& issue, Compute& compute) {
-  asm volatile("s_waitcnt vmcnt(14)\n\ts_barrier" ::: "memory");
-  // Past the last block the refill re-reads the last block (in bounds) into
-  // a stage that is never read again: the issue stays unconditional, which
-  // keeps the compiler's tracking of the loads in flight exact.
-  issue(min(kb + 2, nkb - 1), refill);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  issue(min(kb + 1, nkb - 1), refill);
   compute(cur);
 }
 
@@ -168,7 +174,6 @@ template <int MODE, bool BF16OUT>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[kStageBytes];
 
   Tile t;
   if (!decode_tile<MODE>(g, t)) return;
@@ -176,53 +181,59 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int K = g.k, N = g.n;
   const int nkb = K / BK;
 
   // ---- global->LDS assignment: one wave instruction moves 8 rows x 128 B.
-  // Wave w moves A rows 32w..32w+31 and W rows 64w..64w+63.  Loads are
-  // buffer loads with an LDS destination: a per-lane 32-bit byte offset
-  // (VGPR, fixed for the whole K loop), the K-block offset in an SGPR, the
-  // LDS address in M0, so issuing costs no VALU work.  Byte offsets fit in
-  // 32 bits (the host rejects operands of 2 GiB or more).
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.a, 0, 0x7FFFFFFF, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)t.w, 0, 0x7FFFFFFF, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)g.sa, 0, 0x7FFFFFFF, kRsrcFlags);
-  const __amdgpu_buffer_rsrc_t sw_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)t.sw, 0, 0x7FFFFFFF, kRsrcFlags);
-  uint32_t a_off[4], w_off[8];
+  // Wave w moves rows 32w..32w+31 of both the A and the W tile.  Loads are
+  // buffer loads with an LDS destination.  Each buffer starts at the tile's
+  // first row and its size ends at the operand's last row, so rows past the
+  // operand read as zero (the hardware range check) instead of being
+  // clamped; A and W then share the per-lane row offsets.  The K-block
+  // offset goes in an SGPR, the LDS address in M0: issuing costs no VALU
+  // work.  Offsets fit in 32 bits (the host rejects operands of 2 GiB+).
+  const uint32_t rowb = (uint32_t)K;  // bytes per operand row
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.a + (size_t)t.m0 * rowb), 0, (int)((uint32_t)(g.rows - t.m0) * rowb), kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(t.w + (size_t)t.n0 * rowb), 0, (int)((uint32_t)(N - t.n0) * rowb), kRsrcFlags);
+  uint32_t r_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wave * 4 + i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    a_off[i] = (uint32_t)min(t.m0 + row, t.mend - 1) * (uint32_t)K + 16u * chunk;
+    r_off[i] = (uint32_t)row * rowb + 16u * (uint32_t)((lane & 7) ^ swz(row));
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    w_off[i] = (uint32_t)min(t.n0 + row, N - 1) * (uint32_t)K + 16u * chunk;
+  // scales of the K block: waves 0-3 bring the A scales of rows 64w..64w+63,
+  // waves 4-7 the W scale of columns 64(w-4)..+63 (one value per column, so
+  // all modes share the LDS layout)
+  const uint32_t sblk = (uint32_t)nkb * 4u;  // bytes per scale row
+  const int sidx = (wave & 3) * 64 + lane;
+  __amdgpu_buffer_rsrc_t s_rsrc;
+  uint32_t s_off;
+  if (wave < 4) {
+    s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g.sa + (size_t)t.m0 * nkb), 0,
+                                               (int)((uint32_t)(g.rows - t.m0) * sblk), kRsrcFlags);
+    s_off = (uint32_t)sidx * sblk;
+  } else if (MODE == kWgrad) {
+    s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(t.sw + (size_t)t.n0 * nkb), 0,
+                                               (int)((uint32_t)(N - t.n0) * sblk), kRsrcFlags);
+    s_off = (uint32_t)sidx * sblk;
+  } else {  // one scale row per 128 columns; n0 is a multiple of 256
+    s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(t.sw + (size_t)(t.n0 >> 7) * nkb), 0,
+                                               (int)((uint32_t)((N - t.n0 + 127) >> 7) * sblk), kRsrcFlags);
+    s_off = (uint32_t)(sidx >> 7) * sblk;
   }
-  // scales of the K block: wave w brings the A scales of rows 64(w&1)..+63
-  // (waves 2-3 repeat waves 0-1's load, so every wave issues the same number
-  // of loads per stage) and the W scale of columns 64w..64w+63 (one value per
-  // column, so all modes share the LDS layout)
-  const uint32_t sa_off = (uint32_t)min(t.m0 + (wave & 1) * 64 + lane, t.mend - 1) * (uint32_t)nkb * 4u;
-  const int wcol = min(t.n0 + wave * 64 + lane, N - 1);
-  const uint32_t sw_off = (uint32_t)((MODE == kWgrad) ? wcol : (wcol >> 7)) * (uint32_t)nkb * 4u;
+  const int s_dst = kScaleOff + (wave < 4 ? 0 : BM * 4) + (wave & 3) * 256;
 
   auto issue = [&](int kb, uint8_t* st) {
     const uint32_t kofs = (uint32_t)kb * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, a_off[i], kofs, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + kATileBytes + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + kATileBytes + (wave * 8 + i) * 1024), 16, w_off[i], kofs, 0, 0);
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sa_rsrc, (lds_void_ptr)(st + kScaleOff + (wave & 1) * 256), 4, sa_off, (uint32_t)kb * 4u, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sw_rsrc, (lds_void_ptr)(st + kScaleOff + BM * 4 + wave * 256), 4, sw_off, (uint32_t)kb * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + s_dst), 4, s_off, (uint32_t)kb * 4u, 0, 0);
   };
 
   v4f acc[4][8];
@@ -237,10 +248,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
 
   // One K block: 8 W fragments (j) x 4 M fragments (f) x 4 K steps of 32 (q)
   // = 128 MFMAs per wave.  Explicit software pipeline, in program order:
-  //   - all LDS reads of the block's A fragments and of W fragments 0 and 1
-  //     are issued first; A fragments are widened just in time, q-part by
-  //     q-part, inside W fragment 0, so the first MFMAs wait for 20
-  //     conversions rather than 80;
+  //   - the block's A fragments are read and widened first (the other wave
+  //     of the SIMD keeps the matrix core busy meanwhile), then W fragment 0;
   //   - W fragment j+1 is widened to BF16 during j, q-part by q-part, each
   //     into the slot whose MFMAs have all been issued; each half of its
   //     E4M3 bytes, once widened, is refilled from LDS with fragment j+2's,
@@ -267,21 +276,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       const v4i& r = q < 2 ? lo : hi;
       return e4m3x8_to_bf16(r[(q & 1) * 2], r[(q & 1) * 2 + 1]);
     };
-    v4i w0lo, w0hi, wlo, whi;  // E4M3 bytes of W fragment 0 and of the next one
-    read_w_lo(0, w0lo);
-    read_w_hi(0, w0hi);
-    v4i alo[4], ahi[4];
     float sa[4];
     const int arow0 = wm * 64 + r16;
     const int asw = swz(arow0);  // same swizzle for rows arow0 + 16f
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint8_t* base = st + (arow0 + f * 16) * 128;
-      alo[f] = *reinterpret_cast<const v4i*>(base + 16 * (c0 ^ asw));
-      ahi[f] = *reinterpret_cast<const v4i*>(base + 16 * ((c0 + 1) ^ asw));
-    }
-    read_w_lo(1, wlo);
-    read_w_hi(1, whi);
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
     float sc[4];
@@ -290,9 +287,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
     }
-
     v8bf af[4][4];  // A fragments widened to BF16: [f][q]
-    v8bf bf[4];     // the current W fragment widened to BF16: [q]
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint8_t* base = st + (arow0 + f * 16) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(base + 16 * (c0 ^ asw));
+      const v4i hi = *reinterpret_cast<const v4i*>(base + 16 * ((c0 + 1) ^ asw));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) af[f][q] = part(lo, hi, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    v4i wlo, whi;  // E4M3 bytes of the next W fragment
+    v8bf bf[4];    // the current W fragment widened to BF16: [q]
+    read_w_lo(0, wlo);
+    read_w_hi(0, whi);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bf[q] = part(wlo, whi, q);
+    read_w_lo(1, wlo);
+    read_w_hi(1, whi);
     v4f p[4];
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
@@ -309,12 +321,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (j == 0) {  // widen W fragment 0 and the A fragments just in time
-          bf[q] = part(w0lo, w0hi, q);
-#pragma unroll
-          for (int f = 0; f < 4; ++f) af[f][q] = part(alo[f], ahi[f], q);
-          __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           if (q == 0 && j > 0) fold(j - 1, f);
@@ -335,36 +341,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int f = 0; f < 4; ++f) fold(7, f);
   };
 
-  // Three LDS stages: block kb+2 streams in while kb is multiplied.  Each
-  // wave issues 14 loads per stage and loads complete in order, so at the
-  // top of block kb, vmcnt <= 14 means block kb has landed (block kb+1 is
-  // still in flight); the barrier then makes every wave's part visible and
-  // guarantees the stage being refilled (that of kb-1) is no longer read.
-  if (nkb > 0) {
-    issue(0, stage0);
-    issue(min(1, nkb - 1), stage1);
-  }
-  // The barrier (in run_step) is a bare s_barrier: __syncthreads() would
-  // add a release fence, i.e. vmcnt(0), and wait for block kb+1 too.  It is sufficient
-  // here: each wave's loads of block kb have landed in LDS (vmcnt), and every
-  // LDS read of the stage being refilled was consumed by MFMAs or folds of
-  // the previous block before its wave reached the barrier.  The asm memory
-  // clobber keeps the compiler from moving LDS accesses across it.
+  // Two LDS stages: block kb+1 streams in while kb is multiplied.
+  if (nkb > 0) issue(0, stage0);
   auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
     run_step(kb, nkb, cur, refill, issue, compute);
   };
-  // Main loop without early exits (each stage keeps a fixed buffer, so the
-  // compiler can tell the LDS reads of one stage from the loads into another),
-  // then the remaining one or two blocks.
   int kb = 0;
-  for (; kb + 3 <= nkb; kb += 3) {
-    step(kb, stage0, stage2);
+  for (; kb + 2 <= nkb; kb += 2) {
+    step(kb, stage0, stage1);
     step(kb + 1, stage1, stage0);
-    step(kb + 2, stage2, stage1);
   }
-  if (kb < nkb) step(kb, stage0, stage2);
-  if (kb + 1 < nkb) step(kb + 1, stage1, stage0);
-  // no load may still be writing this workgroup's LDS when its waves exit
+  if (kb < nkb) step(kb, stage0, stage1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds C[m][n..n+3]
