@@ -139,6 +139,104 @@ def quantize_only_rates(torch, fp8q, lib, stream, reps):
     return out
 
 
+def _roofline(flop, nbytes, us):
+    """Time at the roofline max(flop / FP8 peak, bytes / HBM peak) and the
+    fraction of it reached in `us`."""
+    t = max(flop / (FP8_PEAK_TFLOPS * 1e6), nbytes / (HBM_PEAK_GBS * 1e3))
+    return {"us": round(us, 2), "TFLOP/s": round(flop / us / 1e6, 1), "GB/s": round(nbytes / us / 1e3, 1),
+            "flop": flop, "bytes": nbytes, "roofline_us": round(t, 2), "frac_roofline": round(t / us, 4),
+            "bound": "mfma" if flop / (FP8_PEAK_TFLOPS * 1e6) >= nbytes / (HBM_PEAK_GBS * 1e3) else "hbm"}
+
+
+def moe_rates(torch, fp8q, lib, stream, reps):
+    """One GPU's share of the MoE layer: 8192 tokens routed top-8 over 256
+    experts (Zipf(1.1) popularity), 16 hosted experts, one of them empty.
+    Tokens are quantized once (1x128), then their codes and scales are
+    gathered by expert; grouped up-projection 7168 -> 4096 and grouped
+    down-projection 2048 -> 7168, BF16 out."""
+    import synth
+    dev = torch.device("cuda:0")
+    d = synth.moe_grouped()
+    G = len(d["counts"])
+    rows = int(d["counts"].sum())
+
+    def bf(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf(d["x"])
+    xq, xs = fp8q.quantize_act(x)
+    gather = torch.from_numpy(d["gather"]).to(dev)
+    a_up, s_up = xq[gather].contiguous(), xs[gather].contiguous()
+    off = torch.from_numpy(d["offsets"]).to(dev)
+    hq, hs = fp8q.quantize_act(bf(d["h"]))
+    out = {"experts": G, "rows_per_expert": [int(v) for v in d["counts"]], "rows": rows}
+    for name, wname, in_a, in_s in (("up_7168x4096", "w_up", a_up, s_up), ("down_2048x7168", "w_down", hq, hs)):
+        wb = bf(d[wname])
+        g, n, k = wb.shape
+        wq, ws = fp8q.quantize_weight(wb.view(g * n, k))
+        del wb
+        c = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+
+        def fn(i, wq=wq, ws=ws, n=n, k=k, c=c, in_a=in_a, in_s=in_s):
+            return lib.fp8q_grouped_gemm(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
+                                         wq.data_ptr(), ws.data_ptr(), n, k, fp8q.OUT_BF16, c.data_ptr(), n,
+                                         stream.cuda_stream)
+        us = _event_us(torch, stream, fn, reps)
+        flop = 2.0 * rows * n * k
+        nbytes = g * n * k + (g * n // 128) * (k // 128) * 4 + rows * k + rows * (k // 128) * 4 + rows * n * 2
+        r = _roofline(flop, nbytes, us)
+        # sum over experts of each expert's own roofline time (a small
+        # expert is bound by reading its weights)
+        per = 0.0
+        for m in d["counts"]:
+            fe = 2.0 * int(m) * n * k
+            be = n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2)
+            per += max(fe / (FP8_PEAK_TFLOPS * 1e6), be / (HBM_PEAK_GBS * 1e3)) if m else 0.0
+        r["per_expert_roofline_us"] = round(per, 2)
+        out[name] = r
+        del wq, ws, c
+    return out
+
+
+def wgrad_rates(torch, fp8q, lib, stream, reps):
+    """Weight gradient over 16384 tokens: dY 16384 x 2048 and X 16384 x 7168
+    (BF16 ~N(0,1)) quantized in 128-token x 1-feature tiles (codes written
+    feature-major), then dW[2048, 7168] = dY^T X in FP32."""
+    import synth
+    dev = torch.device("cuda:0")
+    d = synth.wgrad()
+    out = {}
+    q = {}
+    for name, arr in (("dy", d["dy"]), ("x", d["x"])):
+        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+        tok, feat = t.shape
+        codes = torch.empty((feat, tok), dtype=torch.uint8, device=dev)
+        scales = torch.empty((feat, tok // 128), dtype=torch.float32, device=dev)
+
+        def fn(i, t=t, tok=tok, feat=feat, codes=codes, scales=scales):
+            return lib.fp8q_quantize_act(t.data_ptr(), tok, feat, feat, fp8q.TILE_TOKEN_T, fp8q.SCALE_FREE,
+                                         codes.data_ptr(), tok, scales.data_ptr(), stream.cuda_stream)
+        us = _event_us(torch, stream, fn, reps)
+        nbytes = tok * feat * 3 + feat * (tok // 128) * 4
+        out[f"quantize_{name}_token_t_{tok}x{feat}"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+                                                        "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                                                        "bytes": nbytes}
+        q[name] = (codes, scales, tok, feat)
+        del t
+    dyc, dys, T, nout = q["dy"]
+    xc, xs, _, kin = q["x"]
+    dw = torch.empty((nout, kin), dtype=torch.float32, device=dev)
+
+    def fg(i):
+        return lib.fp8q_wgrad(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
+                              dw.data_ptr(), kin, stream.cuda_stream)
+    us = _event_us(torch, stream, fg, reps)
+    flop = 2.0 * nout * kin * T
+    nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
+    out[f"wgrad_{nout}x{kin}x{T}"] = _roofline(flop, nbytes, us)
+    return out
+
+
 def _event_us(torch, stream, fn, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn(0)
@@ -247,6 +345,9 @@ def main():
     qw_us = kernel_us(q_wgt_i)
     gemm_us = kernel_us(lambda i: gemm())
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
+    del a_rot, w_rot, ac_rot, wc_rot
+    moe = moe_rates(torch, fp8q, lib, stream, max(3, args.steps // 2))
+    wg = wgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     qa_gbs = ACT_BYTES / (qa_us * 1e-6) / 1e9
     qw_gbs = WGT_BYTES / (qw_us * 1e-6) / 1e9
     gemm_tflops = GEMM_FLOP / (gemm_us * 1e-6) / 1e12
@@ -277,6 +378,8 @@ def main():
                                   "frac_fp8_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
         },
         "quantize_only": quant_only,
+        "moe_grouped": moe,
+        "wgrad": wg,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": GEMM_TRAFFIC_BYTES},
