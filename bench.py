@@ -176,26 +176,33 @@ def moe_rates(torch, fp8q, lib, stream, reps):
         wq, ws = fp8q.quantize_weight(wb.view(g * n, k))
         del wb
         c = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
-
-        def fn(i, wq=wq, ws=ws, n=n, k=k, c=c, in_a=in_a, in_s=in_s):
-            return lib.fp8q_grouped_gemm(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
-                                         wq.data_ptr(), ws.data_ptr(), n, k, fp8q.OUT_BF16, c.data_ptr(), n,
-                                         stream.cuda_stream)
-        us = _event_us(torch, stream, fn, reps)
-        flop = 2.0 * rows * n * k
-        nbytes = g * n * k + (g * n // 128) * (k // 128) * 4 + rows * k + rows * (k // 128) * 4 + rows * n * 2
-        r = _roofline(flop, nbytes, us)
-        # sum over experts of each expert's own roofline time (a small
-        # expert is bound by reading its weights)
-        per = 0.0
-        for m in d["counts"]:
-            fe = 2.0 * int(m) * n * k
-            be = n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2)
-            per += max(fe / (FP8_PEAK_TFLOPS * 1e6), be / (HBM_PEAK_GBS * 1e3)) if m else 0.0
-        r["per_expert_roofline_us"] = round(per, 2)
-        out[name] = r
+        for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
+            out[name + acc_name] = _grouped_rate(torch, lib, stream, reps, d["counts"], in_a, in_s, off, G, rows,
+                                                 wq, ws, n, k, c, acc, fp8q)
         del wq, ws, c
     return out
+
+
+def _grouped_rate(torch, lib, stream, reps, counts, in_a, in_s, off, G, rows, wq, ws, n, k, c, acc, fp8q):
+    """Grouped GEMM time for one accumulation mode, with the whole-kernel and
+    the per-expert roofline."""
+    def fn(i):
+        return lib.fp8q_grouped_gemm(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
+                                     wq.data_ptr(), ws.data_ptr(), n, k, fp8q.OUT_BF16, acc, c.data_ptr(),
+                                     n, stream.cuda_stream)
+    us = _event_us(torch, stream, fn, reps)
+    flop = 2.0 * rows * n * k
+    nbytes = G * n * k + (G * n // 128) * (k // 128) * 4 + rows * k + rows * (k // 128) * 4 + rows * n * 2
+    r = _roofline(flop, nbytes, us)
+    # sum over experts of each expert's own roofline time (a small
+    # expert is bound by reading its weights)
+    per = 0.0
+    for m in counts:
+        fe = 2.0 * int(m) * n * k
+        be = n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2)
+        per += max(fe / (FP8_PEAK_TFLOPS * 1e6), be / (HBM_PEAK_GBS * 1e3)) if m else 0.0
+    r["per_expert_roofline_us"] = round(per, 2)
+    return r
 
 
 def wgrad_rates(torch, fp8q, lib, stream, reps):
@@ -227,13 +234,14 @@ def wgrad_rates(torch, fp8q, lib, stream, reps):
     xc, xs, _, kin = q["x"]
     dw = torch.empty((nout, kin), dtype=torch.float32, device=dev)
 
-    def fg(i):
-        return lib.fp8q_wgrad(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
-                              dw.data_ptr(), kin, stream.cuda_stream)
-    us = _event_us(torch, stream, fg, reps)
     flop = 2.0 * nout * kin * T
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
-    out[f"wgrad_{nout}x{kin}x{T}"] = _roofline(flop, nbytes, us)
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
+        def fg(i, acc=acc):
+            return lib.fp8q_wgrad(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
+                                  acc, dw.data_ptr(), kin, stream.cuda_stream)
+        us = _event_us(torch, stream, fg, reps)
+        out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = _roofline(flop, nbytes, us)
     return out
 
 
@@ -290,7 +298,7 @@ def main():
 
     def gemm():
         return lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
-                             M, N, K, fp8q.OUT_BF16, c.data_ptr(), N, sp)
+                             M, N, K, fp8q.OUT_BF16, fp8q.ACC_FP32, c.data_ptr(), N, sp)
 
     def step():
         st = q_act() | q_wgt() | gemm()
@@ -344,6 +352,9 @@ def main():
     qa_us = kernel_us(q_act_i)
     qw_us = kernel_us(q_wgt_i)
     gemm_us = kernel_us(lambda i: gemm())
+    gemm_f8_us = kernel_us(lambda i: lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
+                                                   w_scales.data_ptr(), M, N, K, fp8q.OUT_BF16,
+                                                   fp8q.ACC_FP8_MFMA, c.data_ptr(), N, sp))
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     del a_rot, w_rot, ac_rot, wc_rot
     moe = moe_rates(torch, fp8q, lib, stream, max(3, args.steps // 2))
@@ -351,6 +362,7 @@ def main():
     qa_gbs = ACT_BYTES / (qa_us * 1e-6) / 1e9
     qw_gbs = WGT_BYTES / (qw_us * 1e-6) / 1e9
     gemm_tflops = GEMM_FLOP / (gemm_us * 1e-6) / 1e12
+    gemm_f8_tflops = GEMM_FLOP / (gemm_f8_us * 1e-6) / 1e12
     value = GEMM_FLOP / (ms_step * 1e-3) / 1e12
 
     out = {
@@ -376,6 +388,11 @@ def main():
                                         "frac_hbm": round(qw_gbs / HBM_PEAK_GBS, 4), "bytes": WGT_BYTES},
             "gemm_block_scaled": {"us": round(gemm_us, 2), "TFLOP/s": round(gemm_tflops, 1),
                                   "frac_fp8_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
+            # the same GEMM with its 128-element partials formed inside the
+            # FP8 matrix core (acc=FP8Q_ACC_FP8_MFMA); not used by the step
+            "gemm_block_scaled_fp8_mfma": {"us": round(gemm_f8_us, 2), "TFLOP/s": round(gemm_f8_tflops, 1),
+                                           "frac_fp8_mfma": round(gemm_f8_tflops / FP8_PEAK_TFLOPS, 4),
+                                           "flop": GEMM_FLOP},
         },
         "quantize_only": quant_only,
         "moe_grouped": moe,

@@ -89,6 +89,8 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
 
 namespace {
 // GEMM kernels address an operand with 32-bit byte offsets.
+bool acc_ok(int acc) { return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA; }
+
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
 
 fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t ld_c, int64_t N) {
@@ -102,10 +104,11 @@ fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t l
 }  // namespace
 
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
-                      int64_t M, int64_t N, int64_t K, int out_dtype, void* c, int64_t ld_c,
+                      int64_t M, int64_t N, int64_t K, int out_dtype, int acc, void* c, int64_t ld_c,
                       hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
+  if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
   if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
@@ -115,14 +118,15 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
   }
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_gemm(a, a_scales, w, w_scales, (int)M, (int)N, (int)K,
-                                    out_dtype == FP8Q_OUT_BF16, c, ld_c, stream));
+                                    out_dtype == FP8Q_OUT_BF16, acc == FP8Q_ACC_FP8_MFMA, c, ld_c, stream));
 }
 
 fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
                               int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N,
-                              int64_t K, int out_dtype, void* c, int64_t ld_c, hipStream_t stream) {
+                              int64_t K, int out_dtype, int acc, void* c, int64_t ld_c, hipStream_t stream) {
   if (G < 0 || !dim_ok(rows_cap) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
+  if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (G == 0 || rows_cap == 0 || N == 0) return FP8Q_OK;
   if (!offsets) return FP8Q_ERR_INVALID_ARG;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
@@ -136,12 +140,15 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int
   if (!aligned16(offsets)) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_grouped_gemm(a, a_scales, offsets, (int)G, (int)rows_cap, w, w_scales, (int)N,
-                                            (int)K, out_dtype == FP8Q_OUT_BF16, c, ld_c, stream));
+                                            (int)K, out_dtype == FP8Q_OUT_BF16, acc == FP8Q_ACC_FP8_MFMA, c,
+                                            ld_c, stream));
 }
 
 fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t, const float* x_scales,
-                       int64_t Nout, int64_t Kin, int64_t T, float* dw, int64_t ld_dw, hipStream_t stream) {
+                       int64_t Nout, int64_t Kin, int64_t T, int acc, float* dw, int64_t ld_dw,
+                       hipStream_t stream) {
   if (!dim_ok(Nout) || !dim_ok(Kin) || !dim_ok(T) || !dim_ok(ld_dw)) return FP8Q_ERR_INVALID_ARG;
+  if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (Nout == 0 || Kin == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(T, FP8Q_OUT_F32, dw, ld_dw, Kin)) return st;
   if (Nout * T >= kMaxOperandBytes || Kin * T >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
@@ -150,7 +157,8 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
     if (!aligned16(dy_t) || !aligned16(x_t) || !aligned16(dy_scales) || !aligned16(x_scales)) return FP8Q_ERR_ALIGN;
   }
   if (fp8q_status st = check_device()) return st;
-  return launched(fp8q::launch_wgrad(dy_t, dy_scales, x_t, x_scales, (int)Nout, (int)Kin, (int)T, dw, ld_dw, stream));
+  return launched(fp8q::launch_wgrad(dy_t, dy_scales, x_t, x_scales, (int)Nout, (int)Kin, (int)T,
+                                     acc == FP8Q_ACC_FP8_MFMA, dw, ld_dw, stream));
 }
 
 }  // extern "C"

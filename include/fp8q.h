@@ -71,6 +71,22 @@ typedef enum fp8q_status {
 
 enum { FP8Q_SCALE_FREE = 0, FP8Q_SCALE_POW2 = 1 };
 enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 };
+/* How each 128-element partial sum of E4M3 products is formed before it is
+ * scaled and added into the FP32 accumulators (tmdrlife.com wr_id=13334 ¶2-¶3,
+ * why-be.co.kr wr_id=35533 ¶4: the FP8 matrix unit keeps its running sum in a
+ * limited width; promotion every 128 elements bounds the damage).
+ *  FP8Q_ACC_FP32: the partial is formed at float32 grade (operands widened
+ *    exactly to BF16, BF16 matrix-core products and float32 sums).  Results
+ *    satisfy |C - exact| <= 1e-5 * sum|a*b| + 1e-6.
+ *  FP8Q_ACC_FP8_MFMA: the partial is formed by the FP8 matrix core itself
+ *    (v_mfma_f32_16x16x128_f8f6f4), twice the FP32 form's throughput.  Measured
+ *    on MI355X: within each aligned group of 8 consecutive products, every
+ *    product is truncated toward zero to a multiple of 2^(E-13), E being the
+ *    exponent of the group's largest product; group sums are then added at
+ *    about float32 grade.  The error of a partial is therefore below
+ *    sum over its 16 groups of 8 * 2^(E_g - 13) plus float32 rounding, and
+ *    can exceed the FP32 form's bound when one product dominates its group. */
+enum { FP8Q_ACC_FP32 = 0, FP8Q_ACC_FP8_MFMA = 1 };
 enum {
   FP8Q_TILE_ROW = 0,    /* 1x128 tiles along cols: codes [rows, ld_codes], scales [rows, ceil(cols/128)] */
   FP8Q_TILE_TOKEN_T = 1 /* 128x1 tiles along rows (the token axis), codes written transposed:
@@ -105,11 +121,12 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
  * a: codes [M, K] contiguous; a_scales [M, K/128]; w: codes [N, K]
  * contiguous; w_scales [ceil(N/128), K/128].  K must be a multiple of 128
  * (K = 0 writes zeros).  out_dtype FP8Q_OUT_F32 (c is float*) or
- * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); row
- * stride ld_c elements.  C is overwritten. */
+ * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); acc
+ * FP8Q_ACC_FP32 or FP8Q_ACC_FP8_MFMA; row stride ld_c elements.  C is
+ * overwritten. */
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       const uint8_t* w, const float* w_scales,
-                      int64_t M, int64_t N, int64_t K, int out_dtype,
+                      int64_t M, int64_t N, int64_t K, int out_dtype, int acc,
                       void* c, int64_t ld_c, hipStream_t stream);
 
 /* Grouped block-scaled GEMM for the MoE experts one device hosts
@@ -123,11 +140,11 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
  *   synchronization); empty groups are allowed;
  * w: codes [G, N, K]; w_scales [G, ceil(N/128), K/128];
  * c: [rows_cap, ld_c] in grouped (expert-sorted) row order; rows not
- * covered by any group are not written. */
+ * covered by any group are not written.  out_dtype and acc as for fp8q_gemm. */
 fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales,
                               const int32_t* offsets, int32_t G, int64_t rows_cap,
                               const uint8_t* w, const float* w_scales,
-                              int64_t N, int64_t K, int out_dtype,
+                              int64_t N, int64_t K, int out_dtype, int acc,
                               void* c, int64_t ld_c, hipStream_t stream);
 
 /* FP8 weight gradient dW[Nout, Kin] = dY^T . X over T tokens
@@ -135,11 +152,11 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales,
  *   dW[n,c] = sum_b dy_scales[n,b] * x_scales[c,b] * sum_{t in block b} dY[t,n] * X[t,c]
  * Operands are FP8Q_TILE_TOKEN_T outputs with ld_codes = T: dy_t codes
  * [Nout, T], dy_scales [Nout, T/128], x_t codes [Kin, T], x_scales
- * [Kin, T/128].  T must be a multiple of 128 (T = 0 writes zeros).
- * Output float32, row stride ld_dw elements, overwritten. */
+ * [Kin, T/128].  T must be a multiple of 128 (T = 0 writes zeros).  acc as
+ * for fp8q_gemm.  Output float32, row stride ld_dw elements, overwritten. */
 fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
                        const uint8_t* x_t, const float* x_scales,
-                       int64_t Nout, int64_t Kin, int64_t T,
+                       int64_t Nout, int64_t Kin, int64_t T, int acc,
                        float* dw, int64_t ld_dw, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */

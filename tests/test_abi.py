@@ -76,28 +76,32 @@ def test_quantize_weight_validation(lib):
 
 def test_gemm_validation(lib):
     g = lib.fp8q_gemm
-    assert g(None, None, None, None, 0, 4, 128, 0, None, 4, None) == fp8q.OK
-    assert g(P16, P16, P16, P16, 4, 4, 100, 0, P16, 4, None) == fp8q.ERR_SHAPE  # K % 128
-    assert g(P16, P16, P16, P16, 4, 4, 128, 2, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(None, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(P16, P16, P16, P16, 4, 8, 128, 0, P16, 4, None) == fp8q.ERR_SHAPE  # ld_c < N
-    assert g(P16, P16, P16, P16, 4, 4, 128, 1, P8, 4, None) == fp8q.ERR_ALIGN
-    assert g(P16, P16, P8, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
-    assert g(P16, P16, P16, P16, 4, 4, -128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(None, None, None, None, 0, 4, 128, 0, 0, None, 4, None) == fp8q.OK
+    assert g(P16, P16, P16, P16, 4, 4, 100, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE  # K % 128
+    assert g(P16, P16, P16, P16, 4, 4, 128, 2, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(None, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(P16, P16, P16, P16, 4, 8, 128, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE  # ld_c < N
+    assert g(P16, P16, P16, P16, 4, 4, 128, 1, 0, P8, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P8, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P16, P16, 4, 4, -128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(P16, P16, P16, P16, 4, 4, 128, 0, 2, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert g(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
 def test_grouped_and_wgrad_validation(lib):
     gg = lib.fp8q_grouped_gemm
-    assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.OK  # no groups
-    assert gg(P16, P16, P16, -1, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert gg(P16, P16, None, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, P16, 4, None) == fp8q.ERR_SHAPE
-    assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.OK  # no groups
+    assert gg(P16, P16, P16, -1, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, None, 2, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE
+    assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_ALIGN
     wg = lib.fp8q_wgrad
-    assert wg(P16, P16, P16, P16, 0, 4, 128, P16, 4, None) == fp8q.OK
-    assert wg(P16, P16, P16, P16, 4, 4, 200, P16, 4, None) == fp8q.ERR_SHAPE
-    assert wg(P16, P16, P16, P16, 4, 8, 128, P16, 4, None) == fp8q.ERR_SHAPE
-    assert wg(P16, None, P16, P16, 4, 4, 128, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert wg(P16, P16, P16, P16, 0, 4, 128, 0, P16, 4, None) == fp8q.OK
+    assert wg(P16, P16, P16, P16, 4, 4, 200, 0, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, P16, P16, P16, 4, 8, 128, 0, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, None, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert wg(P16, P16, P16, P16, 4, 4, 128, 5, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
 def test_valid_calls_reach_the_device_check(lib):
@@ -106,8 +110,9 @@ def test_valid_calls_reach_the_device_check(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
-    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_act(P16, 4, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_DEVICE
     # leading dimensions need no alignment (unaligned strides take element-wise paths)
     assert lib.fp8q_quantize_act(P16, 4, 7, 7, 0, 0, P16, 7, P16, None) == fp8q.ERR_DEVICE
-    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 0, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
