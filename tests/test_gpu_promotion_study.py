@@ -5,7 +5,9 @@ dW = dY^T X over 16384 tokens (dY 16384 x 2048, X 16384 x 7168, BF16
 (64 rows x 64 columns), the error against the exact value is reported for
 
   * the GPU path (libfp8q wgrad: partial sums over 128 tokens, promoted to
-    FP32 with the tile scales) -- measured;
+    FP32 with the tile scales) -- measured, with the partials formed at
+    float32 grade (default) and inside the FP8 matrix core (acc="fp8_mfma"),
+    next to the oracle's model of that unit;
   * emulated accumulators (oracle.accum): a float32 accumulator and a W-bit
     fixed-point accumulator aligned to the running maximum exponent, each
     with promotion every 128 products and with no promotion at all (one
@@ -56,6 +58,7 @@ def test_promotion_study():
     dyq, dysq = fp8q.quantize_act(dev_bf16(d["dy"]), tile_axis="token_t")
     xq, xsq = fp8q.quantize_act(dev_bf16(d["x"]), tile_axis="token_t")
     dw = host(fp8q.wgrad(dyq, dysq, xq, xsq)).astype(np.float64)
+    dw_mfma = host(fp8q.wgrad(dyq, dysq, xq, xsq, acc="fp8_mfma")).astype(np.float64)
 
     rng = np.random.default_rng(2024)
     rsel = np.sort(rng.choice(nout, SAMPLE, replace=False))
@@ -74,7 +77,12 @@ def test_promotion_study():
     exact, s = G.gemm_at(dyc, dys, xc, xs, ri, ci, w_block_rows=False)
 
     report = {"workload": f"dW {nout}x{kin}, T={t}, sample {rows.size} elements",
-              "gpu_interval_128": _stats(dw[rows, cols], exact, s)}
+              "gpu_interval_128": _stats(dw[rows, cols], exact, s),
+              # partials formed inside the FP8 matrix core (limited-width
+              # alignment), promoted every 128 as above
+              "gpu_fp8_mfma_interval_128": _stats(dw_mfma[rows, cols], exact, s)}
+    model, _, _ = accum.gemm_at_mfma(dyc, dys, xc, xs, ri, ci, w_block_rows=False)
+    report["emulated_fp8_mfma_interval_128"] = _stats(model, exact, s)
     say("[study] emulators")
     terms = accum.dequantized_products(dyc[ri], dys[ri], xc[ci], xs[ci])
     report["emulated_fp32_interval_128"] = _stats(accum.accumulate(terms, 128), exact, s)
