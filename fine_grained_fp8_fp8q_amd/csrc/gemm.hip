@@ -37,6 +37,8 @@
 // the same for both operands.  Two LDS stages (66 KiB each): K block kb+1
 // streams in while kb is multiplied; one barrier per K block.  The per-row
 // scales of the K block ride along in the same stage.
+#include <type_traits>
+
 #include "fp8q_internal.h"
 
 namespace fp8q {
@@ -97,6 +99,7 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
 struct Tile {
   int m0, mend;  // rows [m0, mend) of A / C
   int n0;
+  int wrows;     // waves along M: 4 (256-row tile), 2 or 1 (tiles of at most 128 / 64 rows)
   const uint8_t* w;
   const float* sw;
 };
@@ -114,26 +117,37 @@ template <int MODE>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
   const int nkb = g.k / BK;
   if constexpr (MODE == kGrouped) {
-    // Grid = (ceil(rows_cap/128) + groups) * tiles_n, an upper bound of the
+    // Grid = (ceil(rows_cap/256) + groups) * tiles_n, an upper bound of the
     // real tile count; workgroups beyond it exit.  N tiles vary fastest, so
     // the XCD of a workgroup fixes its N tiles and W rows stay XCD-local.
+    // Tiles are handed out longest first: all tiles of more than 128 rows
+    // (every group's full 256-row tiles and long last tiles), then last
+    // tiles of 65-128 rows, then those of 1-64 rows, which run on 2 x 4 and
+    // 1 x 8 wave layouts and fill in as the long tiles finish.
     const int bid = blockIdx.x;
     const int tn = bid % g.tiles_n;
     int mt = bid / g.tiles_n;
-    int gi = 0;
-    for (; gi < g.groups; ++gi) {
-      const int lo = g.offsets[gi], hi = g.offsets[gi + 1];
-      const int cnt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
-      if (mt < cnt) break;
-      mt -= cnt;
+    for (int cls = 0; cls < 3; ++cls) {
+      for (int gi = 0; gi < g.groups; ++gi) {
+        const int lo = g.offsets[gi], hi = g.offsets[gi + 1];
+        const int rows = hi > lo ? hi - lo : 0;
+        const int full = rows / BM, rem = rows % BM;
+        const int cnt = cls == 0 ? full + (rem > 128 ? 1 : 0)
+                      : cls == 1 ? (rem > 64 && rem <= 128 ? 1 : 0)
+                                 : (rem > 0 && rem <= 64 ? 1 : 0);
+        if (mt < cnt) {
+          t.m0 = lo + (cls == 0 ? mt : full) * BM;
+          t.mend = min(t.m0 + BM, hi);
+          t.wrows = cls == 0 ? 4 : cls == 1 ? 2 : 1;
+          t.n0 = tn * BN;
+          t.w = g.w + (int64_t)gi * g.n * g.k;
+          t.sw = g.sw + (int64_t)gi * ((g.n + 127) / 128) * nkb;
+          return true;
+        }
+        mt -= cnt;
+      }
     }
-    if (gi == g.groups) return false;
-    t.m0 = g.offsets[gi] + mt * BM;
-    t.mend = min(t.m0 + BM, (int)g.offsets[gi + 1]);
-    t.n0 = tn * BN;
-    t.w = g.w + (int64_t)gi * g.n * g.k;
-    t.sw = g.sw + (int64_t)gi * ((g.n + 127) / 128) * nkb;
-    return true;
+    return false;
   } else {
     const int logical = xcd_logical(blockIdx.x, gridDim.x);
     const int group = logical / (4 * g.tiles_n);
@@ -144,6 +158,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
     const int tn = in / gm;
     t.m0 = tm * BM;
     t.mend = min(t.m0 + BM, g.rows);
+    t.wrows = 4;
     t.n0 = tn * BN;
     t.w = g.w;
     t.sw = g.sw;
@@ -183,7 +198,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar LDS addresses
-  const int wm = wave & 3, wn = wave >> 2;
+  // waves along M (wave-uniform): 4 x 2 waves of 64 x 128 for a full tile;
+  // 2 x 4 of 64 x 64 or 1 x 8 of 64 x 32 for a grouped tile of <= 128 or
+  // <= 64 rows
+  const int wrows = __builtin_amdgcn_readfirstlane(t.wrows);
+  const int wm = wave & (wrows - 1);
+  const int wn = wave >> (wrows == 4 ? 2 : wrows == 2 ? 1 : 0);
   const int K = g.k, N = g.n;
   const int nkb = K / BK;
 
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[f][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const bool active = (wm * 64 < t.mend - t.m0) && (wn * 128 < N - t.n0);
+  bool active = false;  // set per wave layout below
   const int r16 = lane & 15;
   const int c0 = 2 * (lane >> 4);
 
@@ -262,12 +282,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   //     before the first MFMA of fragment j+1 that overwrites it, 4 MFMAs
   //     after its last one.
   // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
-  auto compute_bf16 = [&](const uint8_t* st, auto& refill_now) {
+  auto compute_bf16 = [&](const uint8_t* st, auto& refill_now, auto jn) {
+    constexpr int JN = decltype(jn)::value;  // 16-column W fragments per wave
+    constexpr int WC = 16 * JN;
     refill_now();
     if (!active) return;
     const float* S = reinterpret_cast<const float*>(st + kScaleOff);
     const uint8_t* Ws = st + kATileBytes;
-    const int wrow0 = wn * 128 + r16;
+    const int wrow0 = wn * WC + r16;
     const int wsw = swz(wrow0);  // same swizzle for rows wrow0 + 16j
     auto read_w_lo = [&](int j, v4i& lo) {
       lo = *reinterpret_cast<const v4i*>(Ws + (wrow0 + j * 16) * 128 + 16 * (c0 ^ wsw));
@@ -286,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
     float sc[4];
     if constexpr (MODE != kWgrad) {
-      const float swv = S[BM + wn * 128];
+      const float swv = S[BM + wn * WC];
 #pragma unroll
       for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
     }
@@ -311,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     v4f p[4];
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
-        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * 128 + j * 16 + 4 * (lane >> 4));
+        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * WC + j * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
@@ -321,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     };
 
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < JN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -332,16 +354,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_barrier(0);
         }
         // slot q is no longer needed by fragment j: widen fragment j+1's part
-        if (j < 7) bf[q] = part(wlo, whi, q);
+        if (j < JN - 1) bf[q] = part(wlo, whi, q);
         // a consumed half of fragment j+1's bytes is refilled with fragment
         // j+2's right away: three MFMA groups before it is needed
-        if (q == 1 && j < 6) read_w_lo(j + 2, wlo);
-        if (q == 3 && j < 6) read_w_hi(j + 2, whi);
+        if (q == 1 && j < JN - 2) read_w_lo(j + 2, wlo);
+        if (q == 3 && j < JN - 2) read_w_hi(j + 2, whi);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) fold(7, f);
+    for (int f = 0; f < 4; ++f) fold(JN - 1, f);
   };
 
   // FP8 matrix-core form: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile
@@ -354,14 +376,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // Per K block: the fragments are read first (W fragment 0, then the four
   // A fragments, then the scales), the refill of the other stage goes out
   // after the first MFMA group, and W fragment j+1 is read while j runs.
-  auto compute_f8 = [&](const uint8_t* st, auto& refill_now) {
+  auto compute_f8 = [&](const uint8_t* st, auto& refill_now, auto jn) {
+    constexpr int JN = decltype(jn)::value;
+    constexpr int WC = 16 * JN;
     if (!active) {
       refill_now();
       return;
     }
     const float* S = reinterpret_cast<const float*>(st + kScaleOff);
     const uint8_t* Ws = st + kATileBytes;
-    const int wrow0 = wn * 128 + r16;
+    const int wrow0 = wn * WC + r16;
     const int wsw = swz(wrow0);
     const int arow0 = wm * 64 + r16;
     const int asw = swz(arow0);
@@ -378,12 +402,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     float sa[4], sc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
-    const float swv = S[BM + wn * 128];
+    const float swv = S[BM + wn * WC];
     __builtin_amdgcn_sched_barrier(0);
     v4f p[4];
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
-        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * 128 + j * 16 + 4 * (lane >> 4));
+        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * WC + j * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
@@ -392,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       }
     };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < 7) wf[(j + 1) & 1] = read8(Ws + (wrow0 + (j + 1) * 16) * 128, wsw);
+    for (int j = 0; j < JN; ++j) {
+      if (j < JN - 1) wf[(j + 1) & 1] = read8(Ws + (wrow0 + (j + 1) * 16) * 128, wsw);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         if (j > 0) fold(j - 1, f);
@@ -411,62 +435,79 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       }
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) fold(7, f);
+    for (int f = 0; f < 4; ++f) fold(JN - 1, f);
   };
 
-  auto compute = [&](const uint8_t* st, auto& refill_now) {
+  auto compute = [&](const uint8_t* st, auto& refill_now, auto jn) {
     if constexpr (F8MFMA) {
-      compute_f8(st, refill_now);
+      compute_f8(st, refill_now, jn);
     } else {
-      compute_bf16(st, refill_now);
+      compute_bf16(st, refill_now, jn);
     }
   };
 
-  // Two LDS stages: block kb+1 streams in while kb is multiplied.
-  if (nkb > 0) issue(0, stage0);
-  auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
-    run_step(kb, nkb, cur, refill, issue, compute);
-  };
-  int kb = 0;
-  for (; kb + 2 <= nkb; kb += 2) {
-    step(kb, stage0, stage1);
-    step(kb + 1, stage1, stage0);
-  }
-  if (kb < nkb) step(kb, stage0, stage1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  auto run = [&](auto jn) {
+    constexpr int JN = decltype(jn)::value;
+    constexpr int WC = 16 * JN;
+    active = (wm * 64 < t.mend - t.m0) && (wn * WC < N - t.n0);
+    // Two LDS stages: block kb+1 streams in while kb is multiplied.
+    if (nkb > 0) issue(0, stage0);
+    auto comp = [&](const uint8_t* st, auto& refill_now) { compute(st, refill_now, jn); };
+    auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
+      run_step(kb, nkb, cur, refill, issue, comp);
+    };
+    int kb = 0;
+    for (; kb + 2 <= nkb; kb += 2) {
+      step(kb, stage0, stage1);
+      step(kb + 1, stage1, stage0);
+    }
+    if (kb < nkb) step(kb, stage0, stage1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: lane holds C[m][n..n+3]
+    // ---- epilogue: lane holds C[m][n..n+3]
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int m = t.m0 + wm * 64 + f * 16 + r16;
-    if (m >= t.mend) continue;
+    for (int f = 0; f < 4; ++f) {
+      const int m = t.m0 + wm * 64 + f * 16 + r16;
+      if (m >= t.mend) continue;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int n = t.n0 + wn * 128 + j * 16 + 4 * (lane >> 4);
-      const v4f r = acc[f][j];
-      if constexpr (BF16OUT) {
-        uint16_t* crow = reinterpret_cast<uint16_t*>(g.c) + (int64_t)m * g.ldc;
-        if (n + 3 < N && g.vec_c) {
-          uint2 pk;
-          pk.x = bf16_rne_bits(r[0]) | (bf16_rne_bits(r[1]) << 16);
-          pk.y = bf16_rne_bits(r[2]) | (bf16_rne_bits(r[3]) << 16);
-          *reinterpret_cast<uint2*>(crow + n) = pk;
+      for (int j = 0; j < JN; ++j) {
+        const int n = t.n0 + wn * WC + j * 16 + 4 * (lane >> 4);
+        const v4f r = acc[f][j];
+        if constexpr (BF16OUT) {
+          uint16_t* crow = reinterpret_cast<uint16_t*>(g.c) + (int64_t)m * g.ldc;
+          if (n + 3 < N && g.vec_c) {
+            uint2 pk;
+            pk.x = bf16_rne_bits(r[0]) | (bf16_rne_bits(r[1]) << 16);
+            pk.y = bf16_rne_bits(r[2]) | (bf16_rne_bits(r[3]) << 16);
+            *reinterpret_cast<uint2*>(crow + n) = pk;
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (n + v < N) crow[n + v] = (uint16_t)bf16_rne_bits(r[v]);
+          }
         } else {
+          float* crow = reinterpret_cast<float*>(g.c) + (int64_t)m * g.ldc;
+          if (n + 3 < N && g.vec_c) {
+            *reinterpret_cast<v4f*>(crow + n) = r;
+          } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n + v < N) crow[n + v] = (uint16_t)bf16_rne_bits(r[v]);
-        }
-      } else {
-        float* crow = reinterpret_cast<float*>(g.c) + (int64_t)m * g.ldc;
-        if (n + 3 < N && g.vec_c) {
-          *reinterpret_cast<v4f*>(crow + n) = r;
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (n + v < N) crow[n + v] = r[v];
+            for (int v = 0; v < 4; ++v)
+              if (n + v < N) crow[n + v] = r[v];
+          }
         }
       }
     }
+  };
+  if constexpr (MODE == kGrouped) {
+    if (wrows == 4) {
+      run(std::integral_constant<int, 8>{});
+    } else if (wrows == 2) {
+      run(std::integral_constant<int, 4>{});
+    } else {
+      run(std::integral_constant<int, 2>{});
+    }
+  } else {
+    run(std::integral_constant<int, 8>{});
   }
 }
 
