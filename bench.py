@@ -248,6 +248,44 @@ def wgrad_rates(torch, fp8q, lib, stream, reps):
     return out
 
 
+def dgrad_rates(torch, fp8q, lib, stream, reps, w):
+    """Activation gradient of the up-projection: the weight W [4096, 7168]
+    quantized once into both orientations (one read, two code copies), then
+    dX [4096, 7168] = dY [4096, 4096] . W (reduction over N = 4096), dY
+    BF16 ~N(0,1) quantized in 1x128 tiles along N, BF16 out."""
+    import synth
+    dev = torch.device("cuda:0")
+    n, k = w.shape
+    m = 4096
+    codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+    codes_t = torch.empty((k, n), dtype=torch.uint8, device=dev)
+    scales_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
+    w2 = [w, w.clone()]
+
+    def fq(i):
+        return lib.fp8q_quantize_weight_t(w2[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, codes.data_ptr(), k,
+                                          scales.data_ptr(), codes_t.data_ptr(), n, scales_t.data_ptr(),
+                                          stream.cuda_stream)
+    us_q = _event_us(torch, stream, fq, reps)
+    qbytes = n * k * 4 + 2 * (n // 128) * (k // 128) * 4
+    out = {"quantize_weight_both_orientations_4096x7168": {
+        "us": round(us_q, 2), "GB/s": round(qbytes / us_q / 1e3, 1),
+        "frac_hbm": round(qbytes / us_q / 1e3 / HBM_PEAK_GBS, 4), "bytes": qbytes}}
+    rng = np.random.default_rng(21)
+    dy = torch.from_numpy(synth.bf16_rne(rng.standard_normal((m, n)).astype(np.float32)).view(np.int16))
+    dyq, dys = fp8q.quantize_act(dy.view(torch.bfloat16).to(dev))
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    flop = 2.0 * m * n * k
+    nbytes = m * n + n * k + m * (n // 128) * 4 + (k // 128) * (n // 128) * 4 + m * k * 2
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
+        def fg(i, acc=acc):
+            return lib.fp8q_gemm(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k,
+                                 n, fp8q.OUT_BF16, acc, dx.data_ptr(), k, stream.cuda_stream)
+        out[f"dgrad_{m}x{k}x{n}{acc_name}"] = _roofline(flop, nbytes, _event_us(torch, stream, fg, reps))
+    return out
+
+
 def _event_us(torch, stream, fn, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn(0)
@@ -363,6 +401,7 @@ def main():
                                                    w_scales.data_ptr(), M, N, K, fp8q.OUT_BF16,
                                                    fp8q.ACC_FP8_MFMA, c.data_ptr(), N, sp))
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
+    dg = dgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4), w)
     del a_rot, w_rot, ac_rot, wc_rot
     moe = moe_rates(torch, fp8q, lib, stream, max(3, args.steps // 2))
     wg = wgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
@@ -407,6 +446,7 @@ def main():
         "quantize_only": quant_only,
         "moe_grouped": moe,
         "wgrad": wg,
+        "dgrad": dg,
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
                      "traffic": GEMM_TRAFFIC_BYTES},

@@ -30,8 +30,8 @@ OUT_F32, OUT_BF16 = 0, 1
 ACC_FP32, ACC_FP8_MFMA = 0, 1
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
-SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm", "fp8q_grouped_gemm",
-           "fp8q_wgrad", "fp8q_status_string")
+SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_weight_t", "fp8q_gemm",
+           "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_status_string")
 
 _lib = None
 
@@ -54,6 +54,7 @@ def load_library(path=None):
     vp, i64, i32, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     lib.fp8q_quantize_act.argtypes = [vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_weight.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp]
+    lib.fp8q_quantize_weight_t.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, vp, vp]
     lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
@@ -164,6 +165,30 @@ def quantize_weight(w, scale_mode="free"):
     return codes, scales
 
 
+def quantize_weight_t(w, scale_mode="free", both=True):
+    """BF16 [N, K] -> (codes, scales, codes_t, scales_t): the 128x128 block
+    quantization of w and its transpose (codes_t [K, N], scales_t
+    [ceil(K/128), ceil(N/128)]) from one pass; with both=False only the
+    transposed pair is written and codes, scales are None.  The transposed
+    pair is the W operand of the activation-gradient GEMM (see dgrad)."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w")
+    ldw = _row_major(w, "w")
+    n, k = w.shape
+    codes = _alloc_codes(n, k, w.device) if both else None
+    scales = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32, device=w.device) \
+        if both else None
+    codes_t = _alloc_codes(k, n, w.device)
+    scales_t = torch.empty(((k + 127) // 128, (n + 127) // 128), dtype=torch.float32, device=w.device)
+    st = load_library().fp8q_quantize_weight_t(
+        _ptr(w), n, k, ldw, _scale_mode(scale_mode),
+        _ptr(codes) if both else None, (codes.stride(0) if codes.numel() else 16) if both else 16,
+        _ptr(scales) if both else None,
+        _ptr(codes_t), codes_t.stride(0) if codes_t.numel() else 16, _ptr(scales_t), _stream(w))
+    _check(st, "fp8q_quantize_weight_t")
+    return codes, scales, codes_t, scales_t
+
+
 def _out_code(dtype):
     torch = _torch()
     if dtype == torch.bfloat16:
@@ -213,6 +238,13 @@ def gemm(a, a_scales, w, w_scales, out_dtype=None, out=None, acc="fp32"):
                                   _out_code(c.dtype), _acc_code(acc), _ptr(c), c.stride(0), _stream(a))
     _check(st, "fp8q_gemm")
     return c
+
+
+def dgrad(dy, dy_scales, w_t, w_t_scales, out_dtype=None, out=None, acc="fp32"):
+    """dX[M, K] = dY[M, N] . W[N, K] from dY quantized in 1x128 tiles along N
+    and the transposed weight pair of quantize_weight_t: the block-scaled
+    GEMM with reduction axis N (fp8q_gemm on those operands)."""
+    return gemm(dy, dy_scales, w_t, w_t_scales, out_dtype=out_dtype, out=out, acc=acc)
 
 
 def grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=None, out=None, acc="fp32"):

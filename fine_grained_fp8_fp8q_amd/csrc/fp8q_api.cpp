@@ -87,6 +87,24 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
                                             scale_mode == FP8Q_SCALE_POW2, codes, ld_codes, scales, stream));
 }
 
+fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w, int scale_mode,
+                                   uint8_t* codes, int64_t ld_codes, float* scales,
+                                   uint8_t* codes_t, int64_t ld_codes_t, float* scales_t, hipStream_t stream) {
+  if (!dim_ok(N) || !dim_ok(K) || !dim_ok(ld_w) || !dim_ok(ld_codes) || !dim_ok(ld_codes_t))
+    return FP8Q_ERR_INVALID_ARG;
+  if (scale_mode != FP8Q_SCALE_FREE && scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return FP8Q_OK;
+  if (!w_bf16 || !codes_t || !scales_t || (codes && !scales)) return FP8Q_ERR_INVALID_ARG;
+  if (ld_w < K || ld_codes_t < N || (codes && ld_codes < K)) return FP8Q_ERR_SHAPE;
+  if (((N + 127) / 128) * ((K + 127) / 128) > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(codes_t) || !aligned16(scales_t)) return FP8Q_ERR_ALIGN;
+  if (codes && (!aligned16(codes) || !aligned16(scales))) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_quant_blocks_t(static_cast<const uint16_t*>(w_bf16), (int)N, (int)K, ld_w,
+                                              scale_mode == FP8Q_SCALE_POW2, codes, ld_codes, scales, codes_t,
+                                              ld_codes_t, scales_t, stream));
+}
+
 namespace {
 // GEMM kernels address an operand with 32-bit byte offsets.
 bool acc_ok(int acc) { return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA; }

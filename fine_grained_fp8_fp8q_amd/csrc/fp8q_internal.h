@@ -16,6 +16,10 @@ hipError_t launch_quant_token_t(const uint16_t* x, int rows, int cols, int64_t l
 hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
                                uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
 
+hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
+                                 uint8_t* codes, int64_t ldc, float* scales, uint8_t* codes_t,
+                                 int64_t ldt, float* scales_t, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                        const float* w_scales, int m, int n, int k, bool bf16_out, bool f8mfma,
                        void* c, int64_t ldc, hipStream_t stream);

@@ -116,6 +116,108 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
   if (tid == 0) scales[blockIdx.x] = ts.s;
 }
 
+// ---------------------------------- 128x128 blocks, plus the transpose ---
+// The same block quantization, also written transposed for the activation
+// gradient dX = dY . W (jp-study.kr doc 258368 ¶3: all three GEMMs of a
+// linear layer run in FP8), whose reduction axis is N: a square block's max-
+// abs does not depend on orientation, so W^T quantized per block is exactly
+// the transpose of W quantized.  Thread t owns the 8x8 sub-block at rows
+// 8(t/16).., columns 8(t%16).., transposes its 64 codes in registers into
+// an LDS copy of the transposed block, which then leaves as whole 128-byte
+// W^T row segments.  `codes` may be null (only the transposed copy is
+// written).
+__device__ __forceinline__ uint32_t byte_of(uint32_t w, int i) { return (w >> (8 * i)) & 0xFFu; }
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __restrict__ w, int n,
+                                                             int k, int64_t ldw,
+                                                             uint8_t* __restrict__ codes, int64_t ldc,
+                                                             float* __restrict__ scales,
+                                                             uint8_t* __restrict__ codes_t, int64_t ldt,
+                                                             float* __restrict__ scales_t, int bn, int bk,
+                                                             bool vec) {
+  constexpr int kTRowBytes = 144;  // 16-byte aligned rows of the transposed block
+  __shared__ uint32_t red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile_t[128 * kTRowBytes];
+  const int tid = threadIdx.x;
+  const int sb = tid & 15;   // column group: columns 8sb..8sb+7 of the block
+  const int sa = tid >> 4;   // row group: rows 8sa..8sa+7
+  const int bi = blockIdx.x / bk;
+  const int bj = blockIdx.x - bi * bk;
+  const int row0 = bi * 128 + 8 * sa, col0 = bj * 128 + 8 * sb;
+  const bool full = vec && (bi * 128 + 128 <= n) && (bj * 128 + 128 <= k);
+
+  uint4 v[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = row0 + p;
+    const uint16_t* src = w + (int64_t)r * ldw + col0;
+    if (full) {
+      v[p] = ld_stream16(src);
+    } else {
+      v[p] = load8_masked(src, r < n ? k - col0 : 0);
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) m = max(m, absmax8(v[p]));
+  m = dpp_max16(m);
+  m = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
+          max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = max(max(red[0], red[1]), max(red[2], red[3]));
+
+  const TileScale ts = tile_scale<POW2>(m);
+  uint2 c[8];  // codes of rows row0 + p, columns col0..col0+7
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    c[p] = encode8<POW2>(v[p], ts);
+    if (codes) {
+      const int r = row0 + p;
+      uint8_t* dst = codes + (int64_t)r * ldc + col0;
+      if (full) {
+        st_stream8(dst, c[p]);
+      } else if (r < n) {
+        store8_masked(dst, c[p], k - col0);
+      }
+    }
+  }
+  // column j of the sub-block (byte j of every row's codes) goes to LDS as
+  // row 8sb + j of the transposed block; the block then leaves as whole
+  // 128-byte W^T row segments (8 lanes per segment, 16 bytes each)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      lo |= byte_of(j < 4 ? c[p].x : c[p].y, j & 3) << (8 * p);
+      hi |= byte_of(j < 4 ? c[p + 4].x : c[p + 4].y, j & 3) << (8 * p);
+    }
+    *reinterpret_cast<uint2*>(&tile_t[(8 * sb + j) * kTRowBytes + 8 * sa]) = make_uint2(lo, hi);
+  }
+  __syncthreads();
+  const int brow0 = bi * 128, bcol0 = bj * 128;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + 256 * i;
+    const int tr = q >> 3, ch = q & 7;   // transposed row (a column of W), 16-byte chunk
+    const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[tr * kTRowBytes + 16 * ch]);
+    const int col = bcol0 + tr;
+    uint8_t* dst = codes_t + (int64_t)col * ldt + brow0 + 16 * ch;
+    if (full) {
+      st_stream16(dst, val);
+    } else if (col < k) {
+      store8_masked(dst, make_uint2(val.x, val.y), n - (brow0 + 16 * ch));
+      store8_masked(dst + 8, make_uint2(val.z, val.w), n - (brow0 + 16 * ch + 8));
+    }
+  }
+  if (tid == 0) {
+    if (scales) scales[blockIdx.x] = ts.s;
+    scales_t[bj * bn + bi] = ts.s;
+  }
+}
+
 // --------------------------------------------- 128x1 token-axis tiles ---
 // Workgroup tile: 128 tokens (rows of x) x 64 features (columns of x).
 // Thread (q = tid/8, c8 = tid%8) loads tokens 4q..4q+3, features 8c8..8c8+7,
@@ -264,6 +366,22 @@ hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, boo
     hipLaunchKernelGGL(quant_blocks_kernel<true>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales, bk, vec);
   } else {
     hipLaunchKernelGGL(quant_blocks_kernel<false>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales, bk, vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
+                                 uint8_t* codes, int64_t ldc, float* scales, uint8_t* codes_t,
+                                 int64_t ldt, float* scales_t, hipStream_t stream) {
+  const int bn = (n + 127) / 128, bk = (k + 127) / 128;
+  const dim3 grid(bn * bk), block(256);
+  const bool vec = ldw % 8 == 0 && (codes == nullptr || ldc % 8 == 0) && ldt % 16 == 0;
+  if (pow2) {
+    hipLaunchKernelGGL(quant_blocks_t_kernel<true>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales,
+                       codes_t, ldt, scales_t, bn, bk, vec);
+  } else {
+    hipLaunchKernelGGL(quant_blocks_t_kernel<false>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales,
+                       codes_t, ldt, scales_t, bn, bk, vec);
   }
   return hipGetLastError();
 }

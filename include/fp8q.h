@@ -115,6 +115,23 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
                                  uint8_t* codes, int64_t ld_codes, float* scales,
                                  hipStream_t stream);
 
+/* The quantization of fp8q_quantize_weight, written for the activation
+ * gradient too (jp-study.kr doc 258368 ¶3: Fprop, Dgrad and Wgrad all take
+ * FP8 inputs).  dX[M,K] = dY[M,N] . W[N,K] reduces over N, so it needs W^T
+ * with N contiguous; a 128x128 block's max-abs does not depend on
+ * orientation, so W^T quantized per block is exactly the transpose of W
+ * quantized, and dX = fp8q_gemm(dY codes, dY scales, codes_t, scales_t) with
+ * dY quantized in 1x128 tiles along N.
+ * codes_t [K, ld_codes_t >= N]; scales_t [ceil(K/128), ceil(N/128)] with
+ * scales_t[j][i] = the scale of block (i, j).  codes/scales (as for
+ * fp8q_quantize_weight) may both be NULL, then only the transposed copy is
+ * written; otherwise both copies come from one read of w. */
+fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w,
+                                   int scale_mode,
+                                   uint8_t* codes, int64_t ld_codes, float* scales,
+                                   uint8_t* codes_t, int64_t ld_codes_t, float* scales_t,
+                                   hipStream_t stream);
+
 /* Block-scaled GEMM C[M,N] = A . W^T (tmdrlife.com wr_id=13334 ¶3;
  * jp-study.kr doc 258368 ¶3):
  *   C[m,n] = sum_b a_scales[m,b] * w_scales[n/128,b] * sum_{k in block b} A[m,k] * W[n,k]

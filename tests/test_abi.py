@@ -88,6 +88,17 @@ def test_gemm_validation(lib):
     assert g(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
+def test_quantize_weight_t_validation(lib):
+    q = lib.fp8q_quantize_weight_t
+    assert q(None, 0, 8, 8, 0, None, 0, None, None, 0, None, None) == fp8q.OK
+    assert q(P16, 4, 8, 8, 0, None, 0, None, None, 16, P16, None) == fp8q.ERR_INVALID_ARG  # codes_t
+    assert q(P16, 4, 8, 8, 0, P16, 16, None, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG   # scales
+    assert q(P16, 4, 8, 8, 2, None, 0, None, P16, 16, P16, None) == fp8q.ERR_INVALID_ARG   # mode
+    assert q(P16, 4, 8, 8, 0, None, 0, None, P16, 3, P16, None) == fp8q.ERR_SHAPE         # ld_codes_t < N
+    assert q(P16, 4, 8, 8, 0, P16, 4, P16, P16, 16, P16, None) == fp8q.ERR_SHAPE          # ld_codes < K
+    assert q(P16, 4, 8, 8, 0, None, 0, None, P8, 16, P16, None) == fp8q.ERR_ALIGN
+
+
 def test_grouped_and_wgrad_validation(lib):
     gg = lib.fp8q_grouped_gemm
     assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.OK  # no groups
@@ -116,3 +127,4 @@ def test_valid_calls_reach_the_device_check(lib):
     assert lib.fp8q_quantize_act(P16, 4, 7, 7, 0, 0, P16, 7, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 0, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_quantize_weight_t(P16, 4, 8, 8, 0, None, 0, None, P16, 16, P16, None) == fp8q.ERR_DEVICE

@@ -234,3 +234,17 @@ def test_pow2_scale_range_edges():
         # q = x / s is exact, so the code is within half an E4M3 ulp of it
         dec = Fraction(float(e4m3.decode(codes)[0, 0]))
         assert abs(dec - ratio) <= Fraction(float(_ulp_e4m3(float(ratio)))) / 2, v
+
+
+@pytest.mark.parametrize("n,k", [(128, 128), (256, 384), (130, 300), (1, 129)])
+@pytest.mark.parametrize("mode", [Q.FREE, Q.POW2])
+def test_weight_blocks_commute_with_transpose(n, k, mode):
+    """A square block's max-abs does not depend on orientation, so quantizing
+    W^T per 128x128 block gives exactly the transpose of W quantized: the
+    reading that lets the activation gradient reuse the weight blocks."""
+    rng = np.random.default_rng(n * 7 + k)
+    w = synth.bf16_rne((rng.standard_normal((n, k)) * np.exp2(rng.integers(-6, 6, (n, k)))).astype(np.float32))
+    c, s = Q.quantize_blocks(w, mode)
+    ct, st = Q.quantize_blocks(np.ascontiguousarray(w.T), mode)
+    assert np.array_equal(ct, c.T)
+    assert np.array_equal(st.view(np.uint32), s.T.view(np.uint32))
