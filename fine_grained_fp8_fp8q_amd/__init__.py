@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_PKG, "libfp8q.so")
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_ALIGN, ERR_LAUNCH, ERR_DEVICE = range(6)
 SCALE_FREE, SCALE_POW2 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-ACC_FP32, ACC_FP8_MFMA = 0, 1
+ACC_FP32, ACC_FP8_MFMA, ACC_FP8_MFMA_SCALED = 0, 1, 2
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
 SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_weight_t", "fp8q_gemm",
@@ -199,12 +199,14 @@ def _out_code(dtype):
 
 
 def _acc_code(acc):
-    """"fp32" (default; partials at float32 grade) or "fp8_mfma" (partials
-    formed inside the FP8 matrix core, ~14-bit alignment in groups of 8)."""
+    """"fp32" (default; partials at float32 grade), "fp8_mfma" (partials
+    formed inside the FP8 matrix core, ~14-bit alignment in groups of 8) or
+    "fp8_mfma_scaled" (power-of-two scales applied by the matrix core, all K
+    blocks accumulated there: no promotion)."""
     try:
-        return {"fp32": ACC_FP32, "fp8_mfma": ACC_FP8_MFMA}[acc]
+        return {"fp32": ACC_FP32, "fp8_mfma": ACC_FP8_MFMA, "fp8_mfma_scaled": ACC_FP8_MFMA_SCALED}[acc]
     except KeyError:
-        raise ValueError('acc must be "fp32" or "fp8_mfma"') from None
+        raise ValueError('acc must be "fp32", "fp8_mfma" or "fp8_mfma_scaled"') from None
 
 
 def _contig_codes(t, name):

@@ -107,7 +107,9 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
 
 namespace {
 // GEMM kernels address an operand with 32-bit byte offsets.
-bool acc_ok(int acc) { return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA; }
+bool acc_ok(int acc) {
+  return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA || acc == FP8Q_ACC_FP8_MFMA_SCALED;
+}
 
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
 
@@ -136,7 +138,7 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
   }
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_gemm(a, a_scales, w, w_scales, (int)M, (int)N, (int)K,
-                                    out_dtype == FP8Q_OUT_BF16, acc == FP8Q_ACC_FP8_MFMA, c, ld_c, stream));
+                                    out_dtype == FP8Q_OUT_BF16, acc, c, ld_c, stream));
 }
 
 fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
@@ -158,7 +160,7 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int
   if (!aligned16(offsets)) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_grouped_gemm(a, a_scales, offsets, (int)G, (int)rows_cap, w, w_scales, (int)N,
-                                            (int)K, out_dtype == FP8Q_OUT_BF16, acc == FP8Q_ACC_FP8_MFMA, c,
+                                            (int)K, out_dtype == FP8Q_OUT_BF16, acc, c,
                                             ld_c, stream));
 }
 
@@ -176,7 +178,7 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
   }
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_wgrad(dy_t, dy_scales, x_t, x_scales, (int)Nout, (int)Kin, (int)T,
-                                     acc == FP8Q_ACC_FP8_MFMA, dw, ld_dw, stream));
+                                     acc, dw, ld_dw, stream));
 }
 
 }  // extern "C"

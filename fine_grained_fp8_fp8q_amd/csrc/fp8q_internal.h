@@ -21,14 +21,14 @@ hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, b
                                  int64_t ldt, float* scales_t, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
-                       const float* w_scales, int m, int n, int k, bool bf16_out, bool f8mfma,
+                       const float* w_scales, int m, int n, int k, bool bf16_out, int acc,
                        void* c, int64_t ldc, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets,
                                int groups, int rows_cap, const uint8_t* w, const float* w_scales,
-                               int n, int k, bool bf16_out, bool f8mfma, void* c, int64_t ldc,
+                               int n, int k, bool bf16_out, int acc, void* c, int64_t ldc,
                                hipStream_t stream);
 hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t,
-                        const float* x_scales, int nout, int kin, int t, bool f8mfma, float* dw,
+                        const float* x_scales, int nout, int kin, int t, int acc, float* dw,
                         int64_t lddw, hipStream_t stream);
 
 }  // namespace fp8q

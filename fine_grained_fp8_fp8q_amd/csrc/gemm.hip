@@ -187,7 +187,7 @@ __device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restr
   compute(cur, refill_now);
 }
 
-template <int MODE, bool BF16OUT, bool F8MFMA>
+template <int MODE, bool BF16OUT, int ACC>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -438,8 +438,61 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int f = 0; f < 4; ++f) fold(JN - 1, f);
   };
 
+  // Hardware-scaled form (power-of-two scales only): the E8M0 exponent of
+  // each operand row's scale rides along with v_mfma_scale_f32_16x16x128_f8f6f4,
+  // which applies it inside the matrix core, and every K block accumulates
+  // into the same matrix-core accumulator -- the pages' "MMA with group
+  // scaling" (tmdrlife.com wr_id=13334 ¶3) and, with it, no promotion: the
+  // running sum never leaves the unit until the epilogue.
+  auto compute_f8s = [&](const uint8_t* st, auto& refill_now, auto jn) {
+    constexpr int JN = decltype(jn)::value;
+    constexpr int WC = 16 * JN;
+    if (!active) {
+      refill_now();
+      return;
+    }
+    const float* S = reinterpret_cast<const float*>(st + kScaleOff);
+    const uint8_t* Ws = st + kATileBytes;
+    const int wrow0 = wn * WC + r16;
+    const int wsw = swz(wrow0);
+    const int arow0 = wm * 64 + r16;
+    const int asw = swz(arow0);
+    auto read8 = [&](const uint8_t* rowp, int sw) {
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp + 16 * (c0 ^ sw));
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + 16 * ((c0 + 1) ^ sw));
+      return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto e8m0 = [](float x) { return (int)((__float_as_uint(x) >> 23) & 0xFFu); };
+    v8i wf[2];
+    wf[0] = read8(Ws + wrow0 * 128, wsw);
+    v8i af[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) af[f] = read8(st + (arow0 + f * 16) * 128, asw);
+    int ae[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ae[f] = e8m0(S[arow0 + f * 16]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+      if (j < JN - 1) wf[(j + 1) & 1] = read8(Ws + (wrow0 + (j + 1) * 16) * 128, wsw);
+      const int we = e8m0(S[BM + wrow0 + j * 16]);  // the scale of this lane's W row
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j & 1], af[f], acc[f][j], 0, 0,
+                                                                     0, we, 0, ae[f]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 0) {
+        refill_now();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   auto compute = [&](const uint8_t* st, auto& refill_now, auto jn) {
-    if constexpr (F8MFMA) {
+    if constexpr (ACC == 2) {
+      compute_f8s(st, refill_now, jn);
+    } else if constexpr (ACC == 1) {
       compute_f8(st, refill_now, jn);
     } else {
       compute_bf16(st, refill_now, jn);
@@ -511,21 +564,23 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   }
 }
 
-template <int MODE, bool F8MFMA>
+template <int MODE, int ACC>
 void launch_out(const GemmArgs& g, int grid, bool bf16_out, hipStream_t stream) {
   if (bf16_out) {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, true, F8MFMA>), dim3(grid), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, true, ACC>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, false, F8MFMA>), dim3(grid), dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, false, ACC>), dim3(grid), dim3(kThreads), 0, stream, g);
   }
 }
 
 template <int MODE>
-hipError_t launch_mode(const GemmArgs& g, int grid, bool bf16_out, bool f8mfma, hipStream_t stream) {
-  if (f8mfma) {
-    launch_out<MODE, true>(g, grid, bf16_out, stream);
+hipError_t launch_mode(const GemmArgs& g, int grid, bool bf16_out, int acc, hipStream_t stream) {
+  if (acc == 2) {
+    launch_out<MODE, 2>(g, grid, bf16_out, stream);
+  } else if (acc == 1) {
+    launch_out<MODE, 1>(g, grid, bf16_out, stream);
   } else {
-    launch_out<MODE, false>(g, grid, bf16_out, stream);
+    launch_out<MODE, 0>(g, grid, bf16_out, stream);
   }
   return hipGetLastError();
 }
@@ -533,37 +588,37 @@ hipError_t launch_mode(const GemmArgs& g, int grid, bool bf16_out, bool f8mfma, 
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
-                       const float* w_scales, int m, int n, int k, bool bf16_out, bool f8mfma,
+                       const float* w_scales, int m, int n, int k, bool bf16_out, int acc,
                        void* c, int64_t ldc, hipStream_t stream) {
   GemmArgs g{};
   g.a = a; g.sa = a_scales; g.w = w; g.sw = w_scales; g.offsets = nullptr;
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
   g.tiles_m = (m + BM - 1) / BM;
   g.tiles_n = (n + BN - 1) / BN;
-  return launch_mode<kDense>(g, g.tiles_m * g.tiles_n, bf16_out, f8mfma, stream);
+  return launch_mode<kDense>(g, g.tiles_m * g.tiles_n, bf16_out, acc, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets,
                                int groups, int rows_cap, const uint8_t* w, const float* w_scales,
-                               int n, int k, bool bf16_out, bool f8mfma, void* c, int64_t ldc,
+                               int n, int k, bool bf16_out, int acc, void* c, int64_t ldc,
                                hipStream_t stream) {
   GemmArgs g{};
   g.a = a; g.sa = a_scales; g.w = w; g.sw = w_scales; g.offsets = offsets;
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = rows_cap; g.n = n; g.k = k; g.groups = groups;
   g.tiles_m = (rows_cap + BM - 1) / BM + groups;  // upper bound of m tiles over all groups
   g.tiles_n = (n + BN - 1) / BN;
-  return launch_mode<kGrouped>(g, g.tiles_m * g.tiles_n, bf16_out, f8mfma, stream);
+  return launch_mode<kGrouped>(g, g.tiles_m * g.tiles_n, bf16_out, acc, stream);
 }
 
 hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t,
-                        const float* x_scales, int nout, int kin, int t, bool f8mfma, float* dw,
+                        const float* x_scales, int nout, int kin, int t, int acc, float* dw,
                         int64_t lddw, hipStream_t stream) {
   GemmArgs g{};
   g.a = dy_t; g.sa = dy_scales; g.w = x_t; g.sw = x_scales; g.offsets = nullptr;
   g.c = dw; g.ldc = lddw; g.vec_c = (lddw % 4) == 0; g.rows = nout; g.n = kin; g.k = t; g.groups = 1;
   g.tiles_m = (nout + BM - 1) / BM;
   g.tiles_n = (kin + BN - 1) / BN;
-  return launch_mode<kWgrad>(g, g.tiles_m * g.tiles_n, false, f8mfma, stream);
+  return launch_mode<kWgrad>(g, g.tiles_m * g.tiles_n, false, acc, stream);
 }
 
 }  // namespace fp8q

@@ -85,8 +85,18 @@ enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 };
  *    exponent of the group's largest product; group sums are then added at
  *    about float32 grade.  The error of a partial is therefore below
  *    sum over its 16 groups of 8 * 2^(E_g - 13) plus float32 rounding, and
- *    can exceed the FP32 form's bound when one product dominates its group. */
-enum { FP8Q_ACC_FP32 = 0, FP8Q_ACC_FP8_MFMA = 1 };
+ *    can exceed the FP32 form's bound when one product dominates its group.
+ *  FP8Q_ACC_FP8_MFMA_SCALED: for power-of-two scales only (FP8Q_SCALE_POW2
+ *    on both operands, every scale in [2^-127, 2^127] or zero): the scales'
+ *    exponents are handed to v_mfma_scale_f32_16x16x128_f8f6f4 as E8M0 block
+ *    scales, so the matrix core applies them itself (tmdrlife.com
+ *    wr_id=13334 ¶3: MMA with group scaling) and every K block accumulates
+ *    in the matrix core's accumulator: no VALU fold and no promotion; the
+ *    in-group alignment of FP8Q_ACC_FP8_MFMA applies, and the running sum
+ *    is added to at about float32 grade once per group of 8 products.
+ *    A scale that is not a power of two is used as the power of two of its
+ *    exponent (results are then wrong). */
+enum { FP8Q_ACC_FP32 = 0, FP8Q_ACC_FP8_MFMA = 1, FP8Q_ACC_FP8_MFMA_SCALED = 2 };
 enum {
   FP8Q_TILE_ROW = 0,    /* 1x128 tiles along cols: codes [rows, ld_codes], scales [rows, ceil(cols/128)] */
   FP8Q_TILE_TOKEN_T = 1 /* 128x1 tiles along rows (the token axis), codes written transposed:
@@ -138,9 +148,8 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
  * a: codes [M, K] contiguous; a_scales [M, K/128]; w: codes [N, K]
  * contiguous; w_scales [ceil(N/128), K/128].  K must be a multiple of 128
  * (K = 0 writes zeros).  out_dtype FP8Q_OUT_F32 (c is float*) or
- * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); acc
- * FP8Q_ACC_FP32 or FP8Q_ACC_FP8_MFMA; row stride ld_c elements.  C is
- * overwritten. */
+ * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); acc one
+ * of the FP8Q_ACC_* forms; row stride ld_c elements.  C is overwritten. */
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       const uint8_t* w, const float* w_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype, int acc,

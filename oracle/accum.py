@@ -107,13 +107,15 @@ def mfma_partials(a_codes_rows, b_codes_rows, group=8, grid_bits=13):
     return tb.sum(axis=2), np.abs(tb).sum(axis=2)
 
 
-def gemm_at_mfma(a_codes, a_scales, w_codes, w_scales, rows, cols, w_block_rows=True):
+def gemm_at_mfma(a_codes, a_scales, w_codes, w_scales, rows, cols, w_block_rows=True, per_block=False):
     """C, S and T at sampled (rows[i], cols[i]) with each block's partial
     formed as ``mfma_partials`` models it, then scaled and summed exactly.
 
     S = sum_b |sa sw| sum_k |a_k w_k| (the GEMM tolerance scale) and
     T = sum_b |sa sw| sum_g |group sum| (the scale of the unit's own
-    float32-grade additions).  Scales as in oracle.gemm.gemm_at.
+    float32-grade additions).  Scales as in oracle.gemm.gemm_at.  With
+    per_block=True the scaled partials and T come back per K block
+    ([samples, K/128]) instead of summed.
     """
     from .e4m3 import decode
     a_codes = np.asarray(a_codes, dtype=np.uint8)
@@ -128,4 +130,6 @@ def gemm_at_mfma(a_codes, a_scales, w_codes, w_scales, rows, cols, w_block_rows=
     wr = cols // 128 if w_block_rows else cols
     sw = np.asarray(w_scales, dtype=np.float32).astype(np.float64)[wr]
     scale = sa * sw
+    if per_block:
+        return scale * p, (np.abs(scale) * pabs).sum(axis=1), np.abs(scale) * t
     return (scale * p).sum(axis=1), (np.abs(scale) * pabs).sum(axis=1), (np.abs(scale) * t).sum(axis=1)

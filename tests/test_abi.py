@@ -84,7 +84,7 @@ def test_gemm_validation(lib):
     assert g(P16, P16, P16, P16, 4, 4, 128, 1, 0, P8, 4, None) == fp8q.ERR_ALIGN
     assert g(P16, P16, P8, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_ALIGN
     assert g(P16, P16, P16, P16, 4, 4, -128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(P16, P16, P16, P16, 4, 4, 128, 0, 2, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert g(P16, P16, P16, P16, 4, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
     assert g(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
