@@ -7,7 +7,9 @@ dW = dY^T X over 16384 tokens (dY 16384 x 2048, X 16384 x 7168, BF16
   * the GPU path (libfp8q wgrad: partial sums over 128 tokens, promoted to
     FP32 with the tile scales) -- measured, with the partials formed at
     float32 grade (default) and inside the FP8 matrix core (acc="fp8_mfma"),
-    next to the oracle's model of that unit;
+    next to the oracle's model of that unit; and, with power-of-two scales,
+    the matrix core applying the scales and keeping the whole sum
+    (acc="fp8_mfma_scaled", no promotion) next to the promoted forms;
   * emulated accumulators (oracle.accum): a float32 accumulator and a W-bit
     fixed-point accumulator aligned to the running maximum exponent, each
     with promotion every 128 products and with no promotion at all (one
@@ -91,6 +93,22 @@ def test_promotion_study():
         report[f"emulated_fixed{w}_interval_128"] = _stats(accum.accumulate(terms, 128, w), exact, s)
         report[f"emulated_fixed{w}_no_promotion"] = _stats(accum.accumulate(terms, t, w), exact, s)
 
+    # the same workload with power-of-two scales, where the matrix core can
+    # apply the scales itself and keep the whole sum: promotion every 128 vs
+    # none, both measured on the GPU
+    say("[study] power-of-two scales: promoted vs unpromoted on the matrix core")
+    dyq2, dys2 = fp8q.quantize_act(dev_bf16(d["dy"]), tile_axis="token_t", scale_mode="pow2")
+    xq2, xs2 = fp8q.quantize_act(dev_bf16(d["x"]), tile_axis="token_t", scale_mode="pow2")
+    dyc2, dysc2 = Q.quantize_token_t(d["dy"][:, rsel], Q.POW2)
+    xc2, xsc2 = Q.quantize_token_t(d["x"][:, csel], Q.POW2)
+    assert_codes_equal(host_codes(dyq2)[rsel], dyc2, "dY codes (pow2)")
+    assert_codes_equal(host_codes(xq2)[csel], xc2, "X codes (pow2)")
+    exact2, s2 = G.gemm_at(dyc2, dysc2, xc2, xsc2, ri, ci, w_block_rows=False)
+    for name, acc in (("fp32_interval_128", "fp32"), ("fp8_mfma_interval_128", "fp8_mfma"),
+                      ("fp8_mfma_scaled_no_promotion", "fp8_mfma_scaled")):
+        got = host(fp8q.wgrad(dyq2, dys2, xq2, xs2, acc=acc)).astype(np.float64)
+        report[f"pow2_gpu_{name}"] = _stats(got[rows, cols], exact2, s2)
+
     say(json.dumps(report, indent=1))
     out = os.environ.get("FP8Q_STUDY_OUT")
     if out:
@@ -99,6 +117,7 @@ def test_promotion_study():
 
     assert report["gpu_interval_128"]["within_tolerance"] == 1.0
     assert report["emulated_fp32_interval_128"]["within_tolerance"] == 1.0
+    assert report["pow2_gpu_fp32_interval_128"]["within_tolerance"] == 1.0
     # promotion is what keeps a narrow accumulator usable: at every width the
     # promoted sum is more accurate than the unpromoted one
     for w in WIDTHS:
