@@ -38,11 +38,10 @@ METRIC = "block-scaled FP8 GEMM TFLOP/s + quantize GB/s, % of MI355X roofline"
 ACT_BYTES = M * K * 2 + M * K + M * (K // 128) * 4
 WGT_BYTES = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
 GEMM_FLOP = 2.0 * M * N * K
-# HBM traffic of one dense GEMM launch (acc=FP32), from rocprofv3 counters:
-# FETCH_SIZE 87,508.8 KiB x 2.000 (a 256 MiB copy reads 131,086.5 KiB) +
-# WRITE_SIZE 32,771.2 KiB x 1.000, for the kernel as it stands; must be
-# re-measured (or set to None) when the GEMM kernel changes
-GEMM_TRAFFIC_BYTES = 212_780_000
+# HBM traffic of one dense GEMM launch (acc=FP32) from rocprofv3 counters
+# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, calibrated on a 256 MiB copy) for
+# the kernel as it stands; None until re-measured after a kernel change
+GEMM_TRAFFIC_BYTES = None
 
 
 def parse():
