@@ -285,18 +285,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   auto compute_bf16 = [&](const uint8_t* st, auto& refill_now, auto jn) {
     constexpr int JN = decltype(jn)::value;  // 16-column W fragments per wave
     constexpr int WC = 16 * JN;
-    refill_now();
+    // Wgrad issues the refill later (see below); the other forms right away
+    if (MODE != kWgrad || !active) refill_now();
     if (!active) return;
     const float* S = reinterpret_cast<const float*>(st + kScaleOff);
     const uint8_t* Ws = st + kATileBytes;
     const int wrow0 = wn * WC + r16;
     const int wsw = swz(wrow0);  // same swizzle for rows wrow0 + 16j
-    auto read_w_lo = [&](int j, v4i& lo) {
-      lo = *reinterpret_cast<const v4i*>(Ws + (wrow0 + j * 16) * 128 + 16 * (c0 ^ wsw));
-    };
-    auto read_w_hi = [&](int j, v4i& hi) {
-      hi = *reinterpret_cast<const v4i*>(Ws + (wrow0 + j * 16) * 128 + 16 * ((c0 + 1) ^ wsw));
-    };
+    // one base address per half; fragment j is 2 KiB further (an
+    // immediate offset of the LDS read)
+    const uint8_t* w_lo = Ws + wrow0 * 128 + 16 * (c0 ^ wsw);
+    const uint8_t* w_hi = Ws + wrow0 * 128 + 16 * ((c0 + 1) ^ wsw);
+    auto read_w_lo = [&](int j, v4i& lo) { lo = *reinterpret_cast<const v4i*>(w_lo + j * 2048); };
+    auto read_w_hi = [&](int j, v4i& hi) { hi = *reinterpret_cast<const v4i*>(w_hi + j * 2048); };
     auto part = [](const v4i& lo, const v4i& hi, int q) {
       const v4i& r = q < 2 ? lo : hi;
       return e4m3x8_to_bf16(r[(q & 1) * 2], r[(q & 1) * 2 + 1]);
@@ -329,12 +330,31 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     v8bf bf[4];      // the current W fragment widened to BF16: [q]
     read_w_lo(0, w0lo);
     read_w_hi(0, w0hi);
+    if constexpr (MODE == kWgrad) {
+      // the Wgrad fold holds more registers: widen up front so the raw
+      // bytes die before the MFMAs start (no spills)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf[q] = part(w0lo, w0hi, q);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) af[f][q] = part(alo[f], ahi[f], q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     read_w_lo(1, wlo);
     read_w_hi(1, whi);
     v4f p[4];
+    // Wgrad: the column scales of fragment j, read once during j (after its
+    // first MFMA group, when fragment j-1's folds are done) and used by j's
+    // folds.  Their address is formed from the per-lane thread index so it
+    // stays one register plus an immediate per fragment (with the
+    // wave-uniform index the compiler keeps one register per fragment and
+    // stage, which spilled).
+    const int wn_lane = (tid >> 6) >> (wrows == 4 ? 2 : wrows == 2 ? 1 : 0);
+    const float* swp = S + BM + wn_lane * WC + 4 * (lane >> 4);
+    v4f swj = v4f{0.f, 0.f, 0.f, 0.f};
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
-        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * WC + j * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
@@ -347,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int j = 0; j < JN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (j == 0) {
+        if (j == 0 && MODE != kWgrad) {
           bf[q] = part(w0lo, w0hi, q);
 #pragma unroll
           for (int f = 0; f < 4; ++f) af[f][q] = part(alo[f], ahi[f], q);
@@ -360,8 +380,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
                                                           q == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : p[f], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // Wgrad (its fold keeps more values live and the compiler spills a
+        // few prologue values) issues the refill of the other stage once the
+        // block's first fragments are in registers: a register reload after
+        // the refill would wait for it (measured 693 -> 460 us for
+        // 2048 x 7168 over 16384 tokens; the dense form is 5% slower so)
+        if (MODE == kWgrad && j == 0 && q == 0) refill_now();
         // slot q is no longer needed by fragment j: widen fragment j+1's part
         if (j < JN - 1) bf[q] = part(wlo, whi, q);
+        if constexpr (MODE == kWgrad) {
+          if (q == 0) swj = *reinterpret_cast<const v4f*>(swp + j * 16);
+        }
         // a consumed half of fragment j+1's bytes is refilled with fragment
         // j+2's right away: three MFMA groups before it is needed
         if (q == 1 && j < JN - 2) read_w_lo(j + 2, wlo);
