@@ -441,9 +441,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     const float swv = S[BM + wn * WC];
     __builtin_amdgcn_sched_barrier(0);
     v4f p[4];
+    // Wgrad: column scales of the fragment being folded, read once per
+    // fragment (after the previous fragment's folds) instead of per fold
+    const float* swp = S + BM + wn * WC + 4 * (lane >> 4);
+    v4f swj = v4f{0.f, 0.f, 0.f, 0.f};
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
-        const v4f swj = *reinterpret_cast<const v4f*>(S + BM + wn * WC + j * 16 + 4 * (lane >> 4));
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
@@ -461,6 +464,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
                                                                0, 0, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (MODE == kWgrad) swj = *reinterpret_cast<const v4f*>(swp + j * 16);
       if (j == 0) {
         refill_now();
         if constexpr (MODE != kWgrad) {
