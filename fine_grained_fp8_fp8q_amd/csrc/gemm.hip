@@ -22,15 +22,15 @@
 //
 // Workgroup tile 256 x 256 x 128, 8 waves (4 along M x 2 along N: two per
 // SIMD, so one wave's LDS waits and conversions overlap the other's MFMAs),
-// wave tile 64 x 128 in at most 256 registers.  The MFMA computes the transposed tile (W rows as its A operand,
-// A rows as its B operand), so each lane owns one output row m and four
-// consecutive columns n: with 1x128 activation scales and 128x128 weight
-// blocks the fold scale a[m] * w[n/128] is one value per lane and per 16-row
-// M fragment.
+// wave tile 64 x 128 in at most 256 registers.  The MFMA computes the
+// transposed tile (W rows as its A operand, A rows as its B operand), so
+// each lane owns one output row m and four consecutive columns n: with 1x128
+// activation scales and 128x128 weight blocks the fold scale a[m] * w[n/128]
+// is one value per lane and per 16-row M fragment.
 //
 // Data movement: both operands are K-contiguous (A [M,K], W [N,K]).  Each
-// 128-byte K slice of a row is moved global->LDS by global_load_lds_dwordx4
-// (no VGPR staging), 8 rows per wave instruction, with the 16-byte chunks of
+// 128-byte K slice of a row is moved global->LDS by buffer_load_dwordx4 with
+// an LDS destination (no VGPR staging), 8 rows per wave instruction, with the 16-byte chunks of
 // a row XOR-swizzled so the fragment reads (ds_read_b128, 16 rows at the
 // same chunk) hit distinct banks.  Lane group g (lanes 16g..16g+15) reads
 // bytes 32g..32g+31 of its row; the k order inside a block only has to be
@@ -53,10 +53,10 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 512;
-constexpr int kATileBytes = BM * BK;                             // 16 KiB
+constexpr int kATileBytes = BM * BK;                             // 32 KiB
 constexpr int kWTileBytes = BN * BK;                             // 32 KiB
-constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [128], W scales [256]
-constexpr int kStageBytes = kScaleOff + (BM + BN) * 4;           // 49.5 KiB
+constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [256], W scales [256]
+constexpr int kStageBytes = kScaleOff + (BM + BN) * 4;           // 66 KiB
 
 enum Mode { kDense = 0, kGrouped = 1, kWgrad = 2 };
 
