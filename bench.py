@@ -154,34 +154,98 @@ def moe_rates(torch, fp8q, lib, stream, reps):
     """One GPU's share of the MoE layer: 8192 tokens routed top-8 over 256
     experts (Zipf(1.1) popularity), 16 hosted experts, one of them empty.
     Tokens are quantized once (1x128), then their codes and scales are
-    gathered by expert; grouped up-projection 7168 -> 4096 and grouped
-    down-projection 2048 -> 7168, BF16 out."""
+    gathered by expert (FP8 dispatch gather); grouped up-projection
+    7168 -> 4096 and grouped down-projection 2048 -> 7168, BF16 out; the
+    SwiGLU between them fused with the 1x128 quantization of its output; and
+    the whole expert FFN forward (gather, up, SwiGLU + quantize, down) as one
+    timed pass."""
     import synth
     dev = torch.device("cuda:0")
     d = synth.moe_grouped()
     G = len(d["counts"])
     rows = int(d["counts"].sum())
+    K_UP = d["x"].shape[1]
 
     def bf(x):
         return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
 
     x = bf(d["x"])
     xq, xs = fp8q.quantize_act(x)
-    gather = torch.from_numpy(d["gather"]).to(dev)
-    a_up, s_up = xq[gather].contiguous(), xs[gather].contiguous()
+    gather = torch.from_numpy(d["gather"].astype(np.int32)).to(dev)
+    a_up, s_up = fp8q.gather_rows(xq, xs, gather)
     off = torch.from_numpy(d["offsets"]).to(dev)
     hq, hs = fp8q.quantize_act(bf(d["h"]))
     out = {"experts": G, "rows_per_expert": [int(v) for v in d["counts"]], "rows": rows}
+
+    # FP8 dispatch gather of the hosted rows
+    nb_up = K_UP // 128
+
+    def fg(i):
+        return lib.fp8q_gather_rows(xq.data_ptr(), xq.shape[0], K_UP, xq.stride(0), xs.data_ptr(),
+                                    gather.data_ptr(), rows, a_up.data_ptr(), a_up.stride(0), s_up.data_ptr(),
+                                    stream.cuda_stream)
+    us = _event_us(torch, stream, fg, reps)
+    gbytes = 2 * rows * (K_UP + nb_up * 4) + rows * 4
+    out["dispatch_gather_fp8"] = {"us": round(us, 2), "GB/s": round(gbytes / us / 1e3, 1),
+                                  "frac_hbm": round(gbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": gbytes}
+
+    # SwiGLU + 1x128 quantization of the up-projection output shape
+    inter = d["w_down"].shape[2]
+    sx = bf(synth.swiglu_input(rows=rows, inter=inter))
+    sq = torch.empty((rows, inter), dtype=torch.uint8, device=dev)
+    ss = torch.empty((rows, inter // 128), dtype=torch.float32, device=dev)
+    cq = torch.empty((rows, 2 * inter), dtype=torch.uint8, device=dev)
+    cs = torch.empty((rows, 2 * inter // 128), dtype=torch.float32, device=dev)
+    for name, cache in (("swiglu_quantize", False), ("swiglu_quantize_with_pow2_cache", True)):
+        def fs(i, cache=cache):
+            return lib.fp8q_swiglu_quantize(sx.data_ptr(), rows, inter, 2 * inter, fp8q.SCALE_FREE,
+                                            sq.data_ptr(), inter, ss.data_ptr(), fp8q.SCALE_POW2,
+                                            cq.data_ptr() if cache else None, 2 * inter,
+                                            cs.data_ptr() if cache else None, stream.cuda_stream)
+        us = _event_us(torch, stream, fs, reps)
+        sbytes = rows * 2 * inter * 2 + rows * inter + rows * (inter // 128) * 4
+        if cache:
+            sbytes += rows * 2 * inter + rows * (2 * inter // 128) * 4
+        out[name] = {"us": round(us, 2), "GB/s": round(sbytes / us / 1e3, 1),
+                     "frac_hbm": round(sbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": sbytes}
+    del sx, cq, cs
+
+    weights = {}
     for name, wname, in_a, in_s in (("up_7168x4096", "w_up", a_up, s_up), ("down_2048x7168", "w_down", hq, hs)):
         wb = bf(d[wname])
         g, n, k = wb.shape
         wq, ws = fp8q.quantize_weight(wb.view(g * n, k))
         del wb
+        weights[wname] = (wq, ws, n, k)
         c = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
         for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
             out[name + acc_name] = _grouped_rate(torch, lib, stream, reps, d["counts"], in_a, in_s, off, G, rows,
                                                  wq, ws, n, k, c, acc, fp8q)
-        del wq, ws, c
+        del c
+
+    # expert FFN forward, default accumulation: dispatch gather -> up ->
+    # SwiGLU + quantize -> down
+    wq_u, ws_u, n_u, k_u = weights["w_up"]
+    wq_d, ws_d, n_d, k_d = weights["w_down"]
+    up_out = torch.empty((rows, n_u), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((rows, n_d), dtype=torch.bfloat16, device=dev)
+
+    def ffn(i):
+        st = fg(i)
+        st = st or lib.fp8q_grouped_gemm(a_up.data_ptr(), s_up.data_ptr(), off.data_ptr(), G, rows,
+                                         wq_u.data_ptr(), ws_u.data_ptr(), n_u, k_u, fp8q.OUT_BF16,
+                                         fp8q.ACC_FP32, up_out.data_ptr(), n_u, stream.cuda_stream)
+        st = st or lib.fp8q_swiglu_quantize(up_out.data_ptr(), rows, inter, n_u, fp8q.SCALE_FREE,
+                                            sq.data_ptr(), inter, ss.data_ptr(), fp8q.SCALE_POW2, None, 0,
+                                            None, stream.cuda_stream)
+        st = st or lib.fp8q_grouped_gemm(sq.data_ptr(), ss.data_ptr(), off.data_ptr(), G, rows,
+                                         wq_d.data_ptr(), ws_d.data_ptr(), n_d, k_d, fp8q.OUT_BF16,
+                                         fp8q.ACC_FP32, y.data_ptr(), n_d, stream.cuda_stream)
+        return st
+    us = _event_us(torch, stream, ffn, reps)
+    flop = 2.0 * rows * (n_u * k_u + n_d * k_d)
+    out["expert_ffn_forward"] = {"us": round(us, 2), "TFLOP/s": round(flop / us / 1e6, 1), "flop": flop,
+                                 "steps": "dispatch gather, grouped up GEMM, SwiGLU + quantize, grouped down GEMM"}
     return out
 
 

@@ -16,6 +16,9 @@ Functions (names follow the C ABI without the ``fp8q_`` prefix):
 * ``gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16|torch.float32)``
 * ``grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=...)``
 * ``wgrad(dy_t, dy_scales, x_t, x_scales)``
+* ``gather_rows(codes, scales, index)`` -> (codes, scales) of rows ``index``
+* ``swiglu_quantize(x, scale_mode=..., cache=False, cache_scale_mode="pow2")``
+  -> (codes, scales[, cache_codes, cache_scales])
 """
 
 import ctypes
@@ -31,7 +34,8 @@ ACC_FP32, ACC_FP8_MFMA, ACC_FP8_MFMA_SCALED = 0, 1, 2
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
 SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_weight_t", "fp8q_gemm",
-           "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_status_string")
+           "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_gather_rows", "fp8q_swiglu_quantize",
+           "fp8q_status_string")
 
 _lib = None
 
@@ -58,6 +62,8 @@ def load_library(path=None):
     lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_gather_rows.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp]
+    lib.fp8q_swiglu_quantize.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, ip, vp, i64, vp, vp]
     for name in SYMBOLS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8q_status_string.argtypes = [ctypes.c_int]
@@ -290,3 +296,64 @@ def wgrad(dy_t, dy_scales, x_t, x_scales, out=None, acc="fp32"):
                                    _acc_code(acc), _ptr(dw), dw.stride(0), _stream(dy_t))
     _check(st, "fp8q_wgrad")
     return dw
+
+
+def gather_rows(codes, scales, index):
+    """FP8 dispatch gather: (codes[index], scales[index]) as new tensors.
+
+    codes uint8 [rows, cols] with contiguous rows (e.g. ``quantize_act``
+    output), scales float32 [rows, ceil(cols/128)] contiguous, index int32
+    [n] on the GPU.  An index outside [0, rows) yields a zero row and a zero
+    scale (the library does not check indices on the host).
+    """
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    ldc = _row_major(codes, "codes")
+    _contig_f32(scales, "scales")
+    _need(index, torch.int32, "index")
+    if index.dim() != 1 or not index.is_contiguous():
+        raise ValueError("index must be a contiguous 1-D int32 tensor")
+    rows, cols = codes.shape
+    nb = (cols + 127) // 128
+    if tuple(scales.shape) != (rows, nb):
+        raise ValueError(f"scales must be [{rows}, {nb}], got {tuple(scales.shape)}")
+    n = index.numel()
+    out = _alloc_codes(n, cols, codes.device)
+    out_s = torch.empty((n, nb), dtype=torch.float32, device=codes.device)
+    st = load_library().fp8q_gather_rows(_ptr(codes), rows, cols, ldc if codes.numel() else cols,
+                                         _ptr(scales), _ptr(index), n, _ptr(out),
+                                         out.stride(0) if out.numel() else _pad16(max(cols, 1)),
+                                         _ptr(out_s), _stream(codes))
+    _check(st, "fp8q_gather_rows")
+    return out, out_s
+
+
+def swiglu_quantize(x, scale_mode="free", cache=False, cache_scale_mode="pow2"):
+    """SwiGLU of x = [gate | up] (BF16 [rows, 2*inter]), quantized 1x128.
+
+    Returns (codes [rows, inter], scales [rows, ceil(inter/128)]); with
+    cache=True also the 1x128 quantization of x itself (cache_scale_mode,
+    inter a multiple of 128): (codes, scales, cache_codes [rows, 2*inter],
+    cache_scales [rows, 2*inter/128]).
+    """
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    ldx = _row_major(x, "x")
+    rows, two_inter = x.shape
+    if two_inter % 2:
+        raise ValueError("x must have an even number of columns (gate | up)")
+    inter = two_inter // 2
+    codes = _alloc_codes(rows, inter, x.device)
+    scales = torch.empty((rows, (inter + 127) // 128), dtype=torch.float32, device=x.device)
+    cc = cs = None
+    if cache:
+        cc = _alloc_codes(rows, two_inter, x.device)
+        cs = torch.empty((rows, (two_inter + 127) // 128), dtype=torch.float32, device=x.device)
+    st = load_library().fp8q_swiglu_quantize(
+        _ptr(x), rows, inter, ldx if x.numel() else two_inter, _scale_mode(scale_mode), _ptr(codes),
+        codes.stride(0) if codes.numel() else _pad16(max(inter, 1)), _ptr(scales),
+        _scale_mode(cache_scale_mode), _ptr(cc) if cache else ctypes.c_void_p(0),
+        cc.stride(0) if cache and cc.numel() else _pad16(max(two_inter, 1)),
+        _ptr(cs) if cache else ctypes.c_void_p(0), _stream(x))
+    _check(st, "fp8q_swiglu_quantize")
+    return (codes, scales, cc, cs) if cache else (codes, scales)

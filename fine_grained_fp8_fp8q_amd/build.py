@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
 
-SOURCES = ["quant.hip", "gemm.hip", "fp8q_api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_api.cpp"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly (the quotient correction and the scale fold depend on it).

@@ -181,4 +181,45 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
                                      acc, dw, ld_dw, stream));
 }
 
+fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld_codes,
+                             const float* scales, const int32_t* index, int64_t n_out, uint8_t* out_codes,
+                             int64_t ld_out, float* out_scales, hipStream_t stream) {
+  if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(ld_codes) || !dim_ok(n_out) || !dim_ok(ld_out))
+    return FP8Q_ERR_INVALID_ARG;
+  if (n_out == 0 || cols == 0) return FP8Q_OK;
+  if (!index || !out_codes || !out_scales) return FP8Q_ERR_INVALID_ARG;
+  if (rows > 0 && (!codes || !scales)) return FP8Q_ERR_INVALID_ARG;
+  if (ld_codes < cols || ld_out < cols) return FP8Q_ERR_SHAPE;
+  if (rows * ld_codes >= kMaxOperandBytes || n_out * ld_out >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
+  if (!aligned16(index) || !aligned16(out_codes) || !aligned16(out_scales)) return FP8Q_ERR_ALIGN;
+  if (rows > 0 && (!aligned16(codes) || !aligned16(scales))) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_gather_rows(codes, (int)rows, (int)cols, ld_codes, scales, index, (int)n_out,
+                                           out_codes, ld_out, out_scales, stream));
+}
+
+fp8q_status fp8q_swiglu_quantize(const void* x_bf16, int64_t rows, int64_t inter, int64_t ld_x, int scale_mode,
+                                 uint8_t* codes, int64_t ld_codes, float* scales, int cache_scale_mode,
+                                 uint8_t* cache_codes, int64_t ld_cache, float* cache_scales,
+                                 hipStream_t stream) {
+  if (!dim_ok(rows) || !dim_ok(inter) || !dim_ok(ld_x) || !dim_ok(ld_codes) || !dim_ok(ld_cache))
+    return FP8Q_ERR_INVALID_ARG;
+  if (scale_mode != FP8Q_SCALE_FREE && scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  const bool cache = cache_codes != nullptr;
+  if (cache && cache_scale_mode != FP8Q_SCALE_FREE && cache_scale_mode != FP8Q_SCALE_POW2)
+    return FP8Q_ERR_INVALID_ARG;
+  if (rows == 0 || inter == 0) return FP8Q_OK;
+  if (!x_bf16 || !codes || !scales || (cache && !cache_scales)) return FP8Q_ERR_INVALID_ARG;
+  if (ld_x < 2 * inter || ld_codes < inter || (cache && ld_cache < 2 * inter)) return FP8Q_ERR_SHAPE;
+  if (cache && inter % 128) return FP8Q_ERR_SHAPE;
+  if (rows * ((inter + 127) / 128) > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
+  if (cache && (!aligned16(cache_codes) || !aligned16(cache_scales))) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_swiglu_quant(static_cast<const uint16_t*>(x_bf16), (int)rows, (int)inter, ld_x,
+                                            scale_mode == FP8Q_SCALE_POW2, codes, ld_codes, scales,
+                                            cache_scale_mode == FP8Q_SCALE_POW2, cache ? cache_codes : nullptr,
+                                            ld_cache, cache ? cache_scales : nullptr, stream));
+}
+
 }  // extern "C"

@@ -31,4 +31,12 @@ hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8
                         const float* x_scales, int nout, int kin, int t, int acc, float* dw,
                         int64_t lddw, hipStream_t stream);
 
+hipError_t launch_gather_rows(const uint8_t* codes, int rows, int cols, int64_t ldc, const float* scales,
+                              const int32_t* index, int n_out, uint8_t* out, int64_t ldo, float* out_scales,
+                              hipStream_t stream);
+// ccodes == nullptr: no cache of the input (cache_pow2, ldcc, cscales unused)
+hipError_t launch_swiglu_quant(const uint16_t* x, int rows, int inter, int64_t ldx, bool pow2, uint8_t* codes,
+                               int64_t ldc, float* scales, bool cache_pow2, uint8_t* ccodes, int64_t ldcc,
+                               float* cscales, hipStream_t stream);
+
 }  // namespace fp8q

@@ -185,6 +185,49 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
                        int64_t Nout, int64_t Kin, int64_t T, int acc,
                        float* dw, int64_t ld_dw, hipStream_t stream);
 
+/* FP8 dispatch gather (jp-study.kr doc 258368 ¶1: activations are quantized
+ * once, before the MoE dispatch, and the FP8 codes travel instead of BF16).
+ * Row i of the output is row index[i] of the quantized activation, codes and
+ * 1x128 scales alike:
+ *   out_codes[i, 0:cols]  = codes[index[i], 0:cols]
+ *   out_scales[i, 0:nb]   = scales[index[i], 0:nb],  nb = ceil(cols/128)
+ * codes [rows, ld_codes >= cols]; scales [rows, nb] (fp8q_quantize_act
+ * output); index: DEVICE int32[n_out] (e.g. the expert-sorted token list of
+ * one device; a token may appear several times).  An index outside
+ * [0, rows) is not checked on the host (that would need a synchronization):
+ * its output row is written as zero codes and a zero scale.  out_codes
+ * [n_out, ld_out >= cols], out_scales [n_out, nb]. */
+fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld_codes,
+                             const float* scales, const int32_t* index, int64_t n_out,
+                             uint8_t* out_codes, int64_t ld_out, float* out_scales,
+                             hipStream_t stream);
+
+/* SwiGLU of the MoE up-projection output, quantized for the down-projection
+ * (tmdrlife.com wr_id=13334 ¶3-¶4: the SwiGLU operator of the MoE sits
+ * between the two FP8 expert GEMMs; its inputs are cached in FP8 with
+ * power-of-two scales and its output is recomputed from them in the
+ * backward pass).  x: BF16 [rows, ld_x >= 2*inter], gate = x[:, 0:inter],
+ * up = x[:, inter:2*inter].  Per element, in float32:
+ *   y = bf16_rne( (g / (1 + exp(-g))) * u )
+ * (the BF16 value an unfused SwiGLU would store), then y is quantized per
+ * 1x128 tile along inter exactly as fp8q_quantize_act(FP8Q_TILE_ROW,
+ * scale_mode) would quantize that BF16 tensor: codes [rows, ld_codes >=
+ * inter], scales [rows, ceil(inter/128)].  exp is float32 with an error of
+ * a few ulp, so y can differ from the correctly rounded BF16 of the exact
+ * value when that value lies within a few float32 ulp of a rounding
+ * boundary between two BF16 numbers.
+ * Optional cache of the input: when cache_codes is not NULL (then
+ * cache_scales must not be NULL either and inter must be a multiple of 128),
+ * x itself is also quantized per 1x128 tile with cache_scale_mode (the
+ * pages' choice is FP8Q_SCALE_POW2): cache_codes [rows, ld_cache >= 2*inter],
+ * cache_scales [rows, 2*inter/128] -- bit for bit what fp8q_quantize_act
+ * writes for x, from the same single read of x.  Inputs must be finite and
+ * every y must be below the largest finite BF16 value. */
+fp8q_status fp8q_swiglu_quantize(const void* x_bf16, int64_t rows, int64_t inter, int64_t ld_x,
+                                 int scale_mode, uint8_t* codes, int64_t ld_codes, float* scales,
+                                 int cache_scale_mode, uint8_t* cache_codes, int64_t ld_cache,
+                                 float* cache_scales, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* fp8q_status_string(fp8q_status s);
 

@@ -4,8 +4,10 @@ TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, obviously correct
 host implementation of what the GPU path computes: the E4M3 codec, the online
 max-abs quantizers (1x128 activation tiles, 128x128 weight blocks, 128x1
 token-axis tiles, free or power-of-two scales), the block-scaled GEMM in its
-dense, grouped and weight-gradient forms, the output acceptance rule, and the
-accumulation emulators used for the promotion-interval report.
+dense, grouped and weight-gradient forms, the output acceptance rule, the
+accumulation emulators used for the promotion-interval report, and the MoE
+glue on either side of the expert GEMMs (FP8 dispatch gather, SwiGLU with
+its 1x128 quantization).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  It shares no code with the HIP library or its
@@ -27,4 +29,4 @@ accumulation emulator beyond its two closed-form special cases, which is
 "parity unpinned" (see ``oracle/accum.py``).
 """
 
-from . import e4m3, quantize, gemm, accum  # noqa: F401
+from . import e4m3, quantize, gemm, accum, moe  # noqa: F401

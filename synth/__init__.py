@@ -23,6 +23,9 @@ Recipes (seed 0; one child stream per tensor from
                  [16, 4096, 7168], down W [16, 7168, 2048] ~N(0, 0.02); the
                  down-projection input is [sum M, 2048] ~N(0,1)
 * Wgrad:         dY 16384x2048 and X 16384x7168 ~N(0,1)
+* SwiGLU input:  the up-projection output of the MoE workload's rows,
+                 [sum M, 4096] (gate | up) ~N(0, 1.7): the spread of a sum
+                 of 7168 N(0,1) x N(0, 0.02) products (sqrt(7168) * 0.02)
 
 Outliers are multiplied in float32 before the BF16 rounding.  "N(0, 0.02)"
 is read as standard deviation 0.02.
@@ -127,3 +130,12 @@ def wgrad(seed=SEED, tokens=16384, nout=2048, kin=7168):
     dy = bf16_rne(normal(r[0], (tokens, nout)))
     x = bf16_rne(normal(r[1], (tokens, kin)))
     return {"dy": dy, "x": x}
+
+
+def swiglu_input(seed=SEED, rows=None, inter=2048):
+    """BF16 [rows, 2*inter] (gate | up) ~N(0, 1.7); rows default to the MoE
+    workload's hosted rows."""
+    if rows is None:
+        rows = int(moe_routing(seed)[1].sum())
+    r = streams(seed + 1, 1)
+    return bf16_rne(normal(r[0], (rows, 2 * inter), 1.7))

@@ -115,6 +115,36 @@ def test_grouped_and_wgrad_validation(lib):
     assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
+def test_gather_rows_validation(lib):
+    g = lib.fp8q_gather_rows
+    # (codes, rows, cols, ld_codes, scales, index, n_out, out, ld_out, out_scales, stream)
+    assert g(None, 10, 64, 64, None, None, 0, None, 64, None, None) == fp8q.OK  # nothing to write
+    assert g(P16, 10, 0, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.OK
+    assert g(P16, -1, 64, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_INVALID_ARG
+    assert g(P16, 10, 64, 64, P16, None, 5, P16, 64, P16, None) == fp8q.ERR_INVALID_ARG  # no index
+    assert g(None, 10, 64, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_INVALID_ARG  # no source
+    assert g(P16, 10, 64, 32, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_SHAPE  # ld_codes < cols
+    assert g(P16, 10, 64, 64, P16, P16, 5, P16, 63, P16, None) == fp8q.ERR_SHAPE  # ld_out < cols
+    assert g(P16, 10, 64, 64, P16, P8, 5, P16, 64, P16, None) == fp8q.ERR_ALIGN
+    assert g(P16, 10, 64, 64, P16, P16, 5, P8, 64, P16, None) == fp8q.ERR_ALIGN
+
+
+def test_swiglu_quantize_validation(lib):
+    f = lib.fp8q_swiglu_quantize
+    # (x, rows, inter, ld_x, mode, codes, ld_codes, scales, cache_mode, cache_codes, ld_cache, cache_scales, stream)
+    assert f(None, 0, 128, 256, 0, None, 128, None, 1, None, 0, None, None) == fp8q.OK
+    assert f(P16, 4, 128, 256, 3, P16, 128, P16, 1, None, 0, None, None) == fp8q.ERR_INVALID_ARG  # mode
+    assert f(P16, 4, 128, 256, 0, P16, 128, P16, 3, P16, 256, P16, None) == fp8q.ERR_INVALID_ARG  # cache mode
+    assert f(P16, 4, 128, 256, 0, None, 128, P16, 1, None, 0, None, None) == fp8q.ERR_INVALID_ARG
+    assert f(P16, 4, 128, 256, 0, P16, 128, P16, 1, P16, 256, None, None) == fp8q.ERR_INVALID_ARG  # cache scales
+    assert f(P16, 4, 128, 255, 0, P16, 128, P16, 1, None, 0, None, None) == fp8q.ERR_SHAPE  # ld_x < 2*inter
+    assert f(P16, 4, 128, 256, 0, P16, 127, P16, 1, None, 0, None, None) == fp8q.ERR_SHAPE
+    assert f(P16, 4, 100, 200, 0, P16, 100, P16, 1, P16, 200, P16, None) == fp8q.ERR_SHAPE  # cache: inter % 128
+    assert f(P16, 4, 128, 256, 0, P16, 128, P16, 1, P16, 255, P16, None) == fp8q.ERR_SHAPE  # ld_cache
+    assert f(P8, 4, 128, 256, 0, P16, 128, P16, 1, None, 0, None, None) == fp8q.ERR_ALIGN
+    assert f(P16, 4, 128, 256, 0, P16, 128, P16, 1, P8, 256, P16, None) == fp8q.ERR_ALIGN
+
+
 def test_valid_calls_reach_the_device_check(lib):
     """Well-formed arguments pass validation; without a gfx950 device the call
     reports FP8Q_ERR_DEVICE and launches nothing."""
@@ -128,3 +158,7 @@ def test_valid_calls_reach_the_device_check(lib):
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 0, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_weight_t(P16, 4, 8, 8, 0, None, 0, None, P16, 16, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gather_rows(P16, 10, 64, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gather_rows(None, 0, 64, 64, None, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_swiglu_quantize(P16, 4, 100, 200, 0, P16, 100, P16, 1, None, 0, None, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_swiglu_quantize(P16, 4, 128, 256, 1, P16, 128, P16, 1, P16, 256, P16, None) == fp8q.ERR_DEVICE

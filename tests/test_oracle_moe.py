@@ -1,0 +1,125 @@
+"""Pins for the oracle's MoE glue (CPU): the FP8 dispatch gather and the
+SwiGLU + 1x128 quantization (jp-study.kr doc 258368 ¶1; tmdrlife.com
+wr_id=13334 ¶3-¶4).
+
+What is checked without re-deriving the oracle's own formulas:
+
+* a hand-worked gather, with repeated and out-of-range indices;
+* gathering the codes of quantized rows equals quantizing the gathered BF16
+  rows (the 1x128 tiles are per row, so dispatching FP8 loses nothing);
+* silu closed forms: silu(0) = 0, sigmoid(ln 3) = 3/4, silu(x) - silu(-x) = x,
+  silu(x) -> x for large x and -> 0 for very negative x;
+* BF16 rounding: hand-worked ties (to even, normal and subnormal) and
+  agreement with the independent float32 -> BF16 rounding on every float32
+  input drawn;
+* SwiGLU with up = 1 and a gate where sigmoid rounds to 1 reduces to the
+  plain 1x128 quantizer of the gate (catches swapped halves), and up = 0
+  gives all-zero tiles with signed zero codes;
+* the acceptance rule accepts the oracle's own output and rejects a planted
+  error in a code or a scale.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import e4m3, moe, quantize as Q
+import synth
+
+
+def _bits(vals):
+    return e4m3.f32_to_bf16_bits_rne(np.asarray(vals, dtype=np.float32))
+
+
+def test_gather_hand_worked():
+    codes = np.array([[1, 2, 3, 4], [5, 6, 7, 8], [9, 10, 11, 12]], dtype=np.uint8)
+    scales = np.array([[0.5], [0.25], [2.0]], dtype=np.float32)
+    c, s = moe.gather_rows(codes, scales, np.array([2, 0, 2, 3, -1, 1], dtype=np.int32))
+    assert c.tolist() == [[9, 10, 11, 12], [1, 2, 3, 4], [9, 10, 11, 12], [0, 0, 0, 0], [0, 0, 0, 0],
+                          [5, 6, 7, 8]]
+    assert s[:, 0].tolist() == [2.0, 0.5, 2.0, 0.0, 0.0, 0.25]
+
+
+def test_gather_commutes_with_row_quantization():
+    rng = np.random.default_rng(3)
+    x = synth.bf16_rne((rng.standard_normal((50, 300)) * np.exp2(rng.integers(-4, 5, (50, 1)))).astype(np.float32))
+    idx = rng.integers(0, 50, 80).astype(np.int32)
+    for mode in (Q.FREE, Q.POW2):
+        c, s = Q.quantize_rows(x, mode)
+        gc, gs = moe.gather_rows(c, s, idx)
+        wc, ws = Q.quantize_rows(x[idx], mode)
+        assert np.array_equal(gc, wc) and np.array_equal(gs, ws)
+
+
+def test_silu_closed_forms():
+    assert moe.silu(0.0) == 0.0
+    ln3 = math.log(3.0)
+    assert moe.silu(ln3) == pytest.approx(0.75 * ln3, rel=1e-15)
+    assert moe.silu(-ln3) == pytest.approx(-0.25 * ln3, rel=1e-15)
+    x = np.random.default_rng(5).standard_normal(1000) * 5
+    assert np.allclose(moe.silu(x) - moe.silu(-x), x, rtol=0, atol=1e-13)
+    assert moe.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(moe.silu(-800.0)) < 1e-300
+
+
+def test_bf16_rounding_ties_and_float32_agreement():
+    hand = [(1 + 2.0 ** -8, 1.0), (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6), (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7),
+            (-(1 + 2.0 ** -8), -1.0), (2.0 ** -134, 0.0), (3 * 2.0 ** -134, 2.0 ** -132),
+            (2.0 ** -133, 2.0 ** -133), (255.5, 256.0), (254.5, 254.0)]
+    for v, want in hand:
+        assert moe.round_bf16(np.array([v]))[0] == want, v
+    rng = np.random.default_rng(11)
+    f = np.concatenate([rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000)),
+                        rng.standard_normal(1000) * 2.0 ** -130]).astype(np.float32)
+    assert np.array_equal(moe.bf16_bits(moe.round_bf16(f.astype(np.float64))), e4m3.f32_to_bf16_bits_rne(f))
+
+
+@pytest.mark.parametrize("mode", [Q.FREE, Q.POW2])
+def test_swiglu_reduces_to_plain_quantizer(mode):
+    rng = np.random.default_rng(7)
+    gate = _bits(40.0 + rng.random((9, 260)) * 60.0)  # sigmoid(g) rounds to 1 in float64 x BF16
+    up = _bits(np.ones((9, 260)))
+    c, s = moe.swiglu_quantize(np.concatenate([gate, up], axis=1), mode)
+    wc, ws = Q.quantize_rows(gate, mode)
+    assert np.array_equal(c, wc) and np.array_equal(s, ws)
+    # up = 0: zero tiles, scale 0, codes keep the sign of silu(g) * 0
+    g2 = _bits(rng.standard_normal((3, 128)))
+    c0, s0 = moe.swiglu_quantize(np.concatenate([g2, _bits(np.zeros((3, 128)))], axis=1), mode)
+    assert np.all(s0 == 0)
+    neg = e4m3.bf16_bits_to_f32(g2) < 0
+    assert np.array_equal(c0, np.where(neg, 0x80, 0x00).astype(np.uint8))
+
+
+def test_accept_rule():
+    rng = np.random.default_rng(13)
+    x = _bits(rng.standard_normal((40, 2 * 333)) * 3)
+    for mode in (Q.FREE, Q.POW2):
+        c, s = moe.swiglu_quantize(x, mode)
+        assert moe.swiglu_accept(x, mode, c, s).all()
+        bad = c.copy()
+        bad[7, 130] ^= 0x01
+        acc = moe.swiglu_accept(x, mode, bad, s)
+        assert not acc[7, 1] and acc.sum() == acc.size - 1
+        bad_s = s.copy()
+        bad_s[2, 0] *= 2
+        assert not moe.swiglu_accept(x, mode, c, bad_s)[2, 0]
+
+
+def test_candidates_only_near_midpoints():
+    """The second candidate differs from the rounded value only within the
+    band around a midpoint, and is then the adjacent BF16 number."""
+    rng = np.random.default_rng(17)
+    x = _bits(rng.standard_normal((64, 2 * 512)) * 2)
+    y = moe.swiglu_exact(x)
+    c1, c2 = moe.swiglu_candidates(x)
+    assert np.array_equal(c1, moe.round_bf16(y))
+    diff = c1 != c2
+    lo, hi, q = moe._bf16_grid(y)
+    assert np.all(np.abs(c1[diff] - c2[diff]) == q[diff])
+    mid = lo + q / 2
+    assert np.all(np.abs(y[diff] - mid[diff]) <= moe.BAND_REL * np.abs(y[diff]) + moe.BAND_ABS)
+    assert 0 < diff.sum() < 0.01 * diff.size
+    # a midpoint between two BF16 numbers and its neighbours on the grid
+    lo, hi, q = moe._bf16_grid(np.array([1 + 2.0 ** -8, -(1 + 2.0 ** -8)]))
+    assert lo.tolist() == [1.0, -(1 + 2.0 ** -7)] and hi.tolist() == [1 + 2.0 ** -7, -1.0]
