@@ -482,6 +482,21 @@ def main():
                                                     wp_codes.data_ptr(), wp_scales.data_ptr(), M, N, K,
                                                     fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA_SCALED, c.data_ptr(), N, sp))
     del ap_codes, ap_scales, wp_codes, wp_scales
+    # the GEMM with its output quantized in the epilogue (1x128 along N, the
+    # FP8 input of a following layer) next to the unfused pair it replaces
+    cq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    cqs = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    gemm_q_us = kernel_us(lambda i: lib.fp8q_gemm_quantized(a_codes.data_ptr(), a_scales.data_ptr(),
+                                                            w_codes.data_ptr(), w_scales.data_ptr(), M, N, K,
+                                                            fp8q.ACC_FP32, fp8q.SCALE_FREE, cq.data_ptr(), N,
+                                                            cqs.data_ptr(), sp))
+
+    def unfused(i):
+        st = gemm()
+        return st or lib.fp8q_quantize_act(c.data_ptr(), M, N, N, fp8q.TILE_ROW, fp8q.SCALE_FREE, cq.data_ptr(),
+                                           N, cqs.data_ptr(), sp)
+    unfused_us = kernel_us(unfused)
+    del cq, cqs
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     dg = dgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4), w)
     del a_rot, w_rot, ac_rot, wc_rot
@@ -530,6 +545,11 @@ def main():
                 "us": round(gemm_f8s_us, 2), "TFLOP/s": round(GEMM_FLOP / gemm_f8s_us / 1e6, 1),
                 "frac_fp8_mfma": round(GEMM_FLOP / gemm_f8s_us / 1e6 / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
         },
+        "gemm_quantized_output": {
+            "workload": "4096x4096x7168 GEMM whose BF16 result is quantized 1x128 along N in the epilogue",
+            "fused_us": round(gemm_q_us, 2), "fused_TFLOP/s": round(GEMM_FLOP / gemm_q_us / 1e6, 1),
+            "unfused_gemm_bf16_plus_quantize_us": round(unfused_us, 2),
+            "hbm_bytes_saved_per_call": M * N * 2 * 2},
         "quantize_only": quant_only,
         "moe_grouped": moe,
         "wgrad": wg,

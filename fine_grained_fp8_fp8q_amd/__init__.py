@@ -16,6 +16,8 @@ Functions (names follow the C ABI without the ``fp8q_`` prefix):
 * ``gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16|torch.float32)``
 * ``grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=...)``
 * ``wgrad(dy_t, dy_scales, x_t, x_scales)``
+* ``gemm_quantized(a, a_scales, w, w_scales, scale_mode=...)`` -> (codes, scales)
+  of C rounded to BF16 and quantized per 1x128 tile along N
 * ``gather_rows(codes, scales, index)`` -> (codes, scales) of rows ``index``
 * ``swiglu_quantize(x, scale_mode=..., cache=False, cache_scale_mode="pow2")``
   -> (codes, scales[, cache_codes, cache_scales])
@@ -34,7 +36,8 @@ ACC_FP32, ACC_FP8_MFMA, ACC_FP8_MFMA_SCALED = 0, 1, 2
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
 SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_weight_t", "fp8q_gemm",
-           "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_gather_rows", "fp8q_swiglu_quantize",
+           "fp8q_gemm_quantized", "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_gather_rows",
+           "fp8q_swiglu_quantize",
            "fp8q_status_string")
 
 _lib = None
@@ -60,6 +63,7 @@ def load_library(path=None):
     lib.fp8q_quantize_weight.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_weight_t.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, vp, vp]
     lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
+    lib.fp8q_gemm_quantized.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
     lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
     lib.fp8q_gather_rows.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp]
@@ -246,6 +250,29 @@ def gemm(a, a_scales, w, w_scales, out_dtype=None, out=None, acc="fp32"):
                                   _out_code(c.dtype), _acc_code(acc), _ptr(c), c.stride(0), _stream(a))
     _check(st, "fp8q_gemm")
     return c
+
+
+def gemm_quantized(a, a_scales, w, w_scales, scale_mode="free", acc="fp32"):
+    """C = A . W^T (as ``gemm``) rounded to BF16 and quantized per 1x128
+    tile along N in the epilogue: (codes uint8 [M, N], scales float32
+    [M, ceil(N/128)]), bit for bit ``quantize_act(gemm(..., bfloat16))``."""
+    torch = _torch()
+    _contig_codes(a, "a")
+    _contig_codes(w, "w")
+    _contig_f32(a_scales, "a_scales")
+    _contig_f32(w_scales, "w_scales")
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("a and w must have the same K")
+    codes = _alloc_codes(m, n, a.device)
+    scales = torch.empty((m, (n + 127) // 128), dtype=torch.float32, device=a.device)
+    st = load_library().fp8q_gemm_quantized(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), m, n, k,
+                                            _acc_code(acc), _scale_mode(scale_mode), _ptr(codes),
+                                            codes.stride(0) if codes.numel() else _pad16(max(n, 1)),
+                                            _ptr(scales), _stream(a))
+    _check(st, "fp8q_gemm_quantized")
+    return codes, scales
 
 
 def dgrad(dy, dy_scales, w_t, w_t_scales, out_dtype=None, out=None, acc="fp32"):

@@ -141,6 +141,28 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                     out_dtype == FP8Q_OUT_BF16, acc, c, ld_c, stream));
 }
 
+fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
+                                int64_t M, int64_t N, int64_t K, int acc, int scale_mode, uint8_t* c_codes,
+                                int64_t ld_c, float* c_scales, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
+  if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
+  if (scale_mode != FP8Q_SCALE_FREE && scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return FP8Q_OK;
+  if (!c_codes || !c_scales) return FP8Q_ERR_INVALID_ARG;
+  if (K % 128) return FP8Q_ERR_SHAPE;
+  if (ld_c < N) return FP8Q_ERR_SHAPE;
+  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || M * ((N + 127) / 128) > kMaxDim)
+    return FP8Q_ERR_SHAPE;
+  if (!aligned16(c_codes) || !aligned16(c_scales)) return FP8Q_ERR_ALIGN;
+  if (K > 0) {
+    if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
+  }
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_gemm_quantized(a, a_scales, w, w_scales, (int)M, (int)N, (int)K, acc,
+                                              scale_mode == FP8Q_SCALE_POW2, c_codes, ld_c, c_scales, stream));
+}
+
 fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
                               int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N,
                               int64_t K, int out_dtype, int acc, void* c, int64_t ld_c, hipStream_t stream) {

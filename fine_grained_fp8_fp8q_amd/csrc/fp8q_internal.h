@@ -23,6 +23,10 @@ hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, b
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                        const float* w_scales, int m, int n, int k, bool bf16_out, int acc,
                        void* c, int64_t ldc, hipStream_t stream);
+// C = A . W^T rounded to BF16, quantized per 1x128 tile along N
+hipError_t launch_gemm_quantized(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                                 const float* w_scales, int m, int n, int k, int acc, bool pow2,
+                                 uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets,
                                int groups, int rows_cap, const uint8_t* w, const float* w_scales,
                                int n, int k, bool bf16_out, int acc, void* c, int64_t ldc,

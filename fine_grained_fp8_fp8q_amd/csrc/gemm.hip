@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "fp8q_internal.h"
+#include "quant_common.h"
 
 namespace fp8q {
 namespace {
@@ -59,6 +60,9 @@ constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [25
 constexpr int kStageBytes = kScaleOff + (BM + BN) * 4;           // 66 KiB
 
 enum Mode { kDense = 0, kGrouped = 1, kWgrad = 2 };
+// Output forms: float32, BF16 (RNE), or the BF16 value quantized per 1x128
+// tile along N to E4M3 codes plus float32 scales (free or power-of-two).
+enum Out { kOutF32 = 0, kOutBF16 = 1, kOutE4M3 = 2, kOutE4M3Pow2 = 3 };
 
 // Buffer resource word 3 for raw (untyped, unswizzled) buffer access.
 constexpr int kRsrcFlags = 0x00020000;
@@ -71,6 +75,7 @@ struct GemmArgs {
   const int32_t* offsets; // grouped: [groups + 1]
   void* c;
   int64_t ldc;
+  float* cs;              // quantized output: scales [rows, ceil(n/128)]
   bool vec_c;             // ldc % 4 == 0: 16-byte (f32) / 8-byte (bf16) row-fragment stores
   int rows;               // dense: M; grouped: rows_cap; wgrad: Nout
   int n, k, groups;
@@ -82,10 +87,6 @@ struct GemmArgs {
 // cover 16 distinct chunk slots across a pair of rows.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Eight E4M3 codes (two dwords, byte order) -> eight BF16 values, exactly.
 __device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
@@ -187,7 +188,7 @@ __device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restr
   compute(cur, refill_now);
 }
 
-template <int MODE, bool BF16OUT, int ACC>
+template <int MODE, int OUT, int ACC>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
@@ -558,6 +559,54 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: lane holds C[m][n..n+3]
+    if constexpr (OUT == kOutE4M3 || OUT == kOutE4M3Pow2) {
+      // The BF16 value of each output, quantized per 1x128 tile along N:
+      // the wave's 128 columns are one tile (dense: WC = 128 and n0 a
+      // multiple of 256), held by the four lanes that share r16, 32 values
+      // each.  Tile max-abs over BF16 magnitude bits, reduced across those
+      // lanes with every lane of the wave active; the scale and the codes
+      // then come from the 1x128 quantizer's own helpers.
+      static_assert(WC == 128, "one 1x128 tile per wave and row");
+      constexpr bool P2 = OUT == kOutE4M3Pow2;
+      const int nbc = (N + 127) >> 7;
+      const int tn0 = t.n0 + wn * WC;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int m = t.m0 + wm * 64 + f * 16 + r16;
+        uint32_t bits[JN][4];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int n = tn0 + j * 16 + 4 * (lane >> 4) + v;
+            bits[j][v] = n < N ? bf16_rne_bits(acc[f][j][v]) : 0u;
+            amax = max(amax, bits[j][v] & 0x7FFFu);
+          }
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+        const TileScale ts = tile_scale<P2>(amax);
+        uint8_t* crow = reinterpret_cast<uint8_t*>(g.c) + (int64_t)m * g.ldc;
+        with_quotient<P2>(ts, [&](auto q) {
+          if (m >= t.mend) return;
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            const int n = tn0 + j * 16 + 4 * (lane >> 4);
+            const uint32_t c4 = pack4_e4m3(q(__uint_as_float(bits[j][0] << 16)), q(__uint_as_float(bits[j][1] << 16)),
+                                           q(__uint_as_float(bits[j][2] << 16)), q(__uint_as_float(bits[j][3] << 16)));
+            if (n + 3 < N && g.vec_c) {
+              *reinterpret_cast<uint32_t*>(crow + n) = c4;
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (n + v < N) crow[n + v] = (uint8_t)(c4 >> (8 * v));
+            }
+          }
+          if ((lane >> 4) == 0 && tn0 < N) g.cs[(int64_t)m * nbc + (tn0 >> 7)] = ts.s;
+        });
+      }
+    } else {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int m = t.m0 + wm * 64 + f * 16 + r16;
@@ -566,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       for (int j = 0; j < JN; ++j) {
         const int n = t.n0 + wn * WC + j * 16 + 4 * (lane >> 4);
         const v4f r = acc[f][j];
-        if constexpr (BF16OUT) {
+        if constexpr (OUT == kOutBF16) {
           uint16_t* crow = reinterpret_cast<uint16_t*>(g.c) + (int64_t)m * g.ldc;
           if (n + 3 < N && g.vec_c) {
             uint2 pk;
@@ -590,6 +639,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
         }
       }
     }
+    }
   };
   if constexpr (MODE == kGrouped) {
     if (wrows == 4) {
@@ -604,23 +654,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   }
 }
 
-template <int MODE, int ACC>
-void launch_out(const GemmArgs& g, int grid, bool bf16_out, hipStream_t stream) {
-  if (bf16_out) {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, true, ACC>), dim3(grid), dim3(kThreads), 0, stream, g);
-  } else {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, false, ACC>), dim3(grid), dim3(kThreads), 0, stream, g);
-  }
-}
-
-template <int MODE>
-hipError_t launch_mode(const GemmArgs& g, int grid, bool bf16_out, int acc, hipStream_t stream) {
+template <int MODE, int OUT>
+hipError_t launch_acc(const GemmArgs& g, int grid, int acc, hipStream_t stream) {
   if (acc == 2) {
-    launch_out<MODE, 2>(g, grid, bf16_out, stream);
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 2>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else if (acc == 1) {
-    launch_out<MODE, 1>(g, grid, bf16_out, stream);
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 1>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else {
-    launch_out<MODE, 0>(g, grid, bf16_out, stream);
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 0>), dim3(grid), dim3(kThreads), 0, stream, g);
   }
   return hipGetLastError();
 }
@@ -635,7 +676,22 @@ hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
   g.tiles_m = (m + BM - 1) / BM;
   g.tiles_n = (n + BN - 1) / BN;
-  return launch_mode<kDense>(g, g.tiles_m * g.tiles_n, bf16_out, acc, stream);
+  const int grid = g.tiles_m * g.tiles_n;
+  return bf16_out ? launch_acc<kDense, kOutBF16>(g, grid, acc, stream)
+                  : launch_acc<kDense, kOutF32>(g, grid, acc, stream);
+}
+
+hipError_t launch_gemm_quantized(const uint8_t* a, const float* a_scales, const uint8_t* w,
+                                 const float* w_scales, int m, int n, int k, int acc, bool pow2,
+                                 uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
+  GemmArgs g{};
+  g.a = a; g.sa = a_scales; g.w = w; g.sw = w_scales; g.offsets = nullptr;
+  g.c = codes; g.ldc = ldc; g.cs = scales; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
+  g.tiles_m = (m + BM - 1) / BM;
+  g.tiles_n = (n + BN - 1) / BN;
+  const int grid = g.tiles_m * g.tiles_n;
+  return pow2 ? launch_acc<kDense, kOutE4M3Pow2>(g, grid, acc, stream)
+              : launch_acc<kDense, kOutE4M3>(g, grid, acc, stream);
 }
 
 hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets,
@@ -647,7 +703,9 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = rows_cap; g.n = n; g.k = k; g.groups = groups;
   g.tiles_m = (rows_cap + BM - 1) / BM + groups;  // upper bound of m tiles over all groups
   g.tiles_n = (n + BN - 1) / BN;
-  return launch_mode<kGrouped>(g, g.tiles_m * g.tiles_n, bf16_out, acc, stream);
+  const int grid = g.tiles_m * g.tiles_n;
+  return bf16_out ? launch_acc<kGrouped, kOutBF16>(g, grid, acc, stream)
+                  : launch_acc<kGrouped, kOutF32>(g, grid, acc, stream);
 }
 
 hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t,
@@ -658,7 +716,7 @@ hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8
   g.c = dw; g.ldc = lddw; g.vec_c = (lddw % 4) == 0; g.rows = nout; g.n = kin; g.k = t; g.groups = 1;
   g.tiles_m = (nout + BM - 1) / BM;
   g.tiles_n = (kin + BN - 1) / BN;
-  return launch_mode<kWgrad>(g, g.tiles_m * g.tiles_n, false, acc, stream);
+  return launch_acc<kWgrad, kOutF32>(g, g.tiles_m * g.tiles_n, acc, stream);
 }
 
 }  // namespace fp8q

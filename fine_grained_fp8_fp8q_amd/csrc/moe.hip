@@ -82,11 +82,6 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return (g * sg) * u;
 }
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Eight (gate, up) BF16 pairs -> eight BF16 SwiGLU values in chunk layout.
 __device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
   const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
@@ -94,8 +89,8 @@ __device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
   uint32_t y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = bf16_bits_rne(swiglu(bf16_lo(gw[i]), bf16_lo(uw[i])));
-    const uint32_t hi = bf16_bits_rne(swiglu(bf16_hi(gw[i]), bf16_hi(uw[i])));
+    const uint32_t lo = bf16_rne_bits(swiglu(bf16_lo(gw[i]), bf16_lo(uw[i])));
+    const uint32_t hi = bf16_rne_bits(swiglu(bf16_hi(gw[i]), bf16_hi(uw[i])));
     y[i] = lo | (hi << 16);
   }
   return make_uint4(y[0], y[1], y[2], y[3]);

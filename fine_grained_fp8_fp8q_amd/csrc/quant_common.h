@@ -55,6 +55,12 @@ __device__ __forceinline__ uint32_t dpp_max16(uint32_t v) {
   return v;
 }
 
+// float32 -> BF16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -155,34 +161,36 @@ __device__ __forceinline__ TileScale tile_scale(uint32_t amax_bits) {
   }
 }
 
-// Eight BF16 values (one 16-byte chunk) -> eight codes (two words), with the
-// quotient form chosen by Q (quotient<POW2> or a Markstein-only free form).
-template <class Q>
-__device__ __forceinline__ uint2 encode8_with(uint4 v, Q q) {
-  uint2 r;
-  r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
-  r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
-  return r;
-}
-
-// Eight BF16 values -> eight codes.  Free scales: the per-element IEEE
-// division of a tiny-amax tile is taken only when some lane of the wave
-// holds such a tile (a wave-uniform branch), so the common case is the bare
-// Markstein quotient with no per-element branching.
-template <bool POW2>
-__device__ __forceinline__ uint2 encode8(uint4 v, const TileScale& t) {
+// Runs body(q) with q(x) = the tile quotient of x.  Free scales: the
+// per-element IEEE division of a tiny-amax tile is taken only when some lane
+// of the wave holds such a tile (a wave-uniform branch: call it with every
+// lane of the wave active), so the common case is the bare Markstein
+// quotient with no per-element branching.
+template <bool POW2, class Body>
+__device__ __forceinline__ auto with_quotient(const TileScale& t, Body body) {
   if constexpr (POW2) {
-    return encode8_with(v, [&](float x) { return quotient<true>(x, t); });
+    return body([&](float x) { return quotient<true>(x, t); });
   } else {
     if (__builtin_amdgcn_ballot_w64(t.slow) == 0) {
-      return encode8_with(v, [&](float x) {
+      return body([&](float x) {
         const float q0 = x * t.mul;
         const float e = __builtin_fmaf(-q0, t.div, x);
         return __builtin_copysignf(__builtin_fmaf(e, t.mul, q0), x);
       });
     }
-    return encode8_with(v, [&](float x) { return quotient_free(x, t); });
+    return body([&](float x) { return quotient_free(x, t); });
   }
+}
+
+// Eight BF16 values (one 16-byte chunk) -> eight codes (two words).
+template <bool POW2>
+__device__ __forceinline__ uint2 encode8(uint4 v, const TileScale& t) {
+  return with_quotient<POW2>(t, [&](auto q) {
+    uint2 r;
+    r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
+    r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
+    return r;
+  });
 }
 
 // Loads up to 8 BF16 values (nvalid may be <= 0 or >= 8); missing ones are +0.

@@ -155,6 +155,23 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype, int acc,
                       void* c, int64_t ld_c, hipStream_t stream);
 
+/* fp8q_gemm with its output quantized in the epilogue, for a consumer that
+ * takes FP8 input (tmdrlife.com wr_id=13334 ¶1: the BF16 output of one
+ * computation is read back from HBM only to be quantized, written as FP8 and
+ * read again for the next MMA; here the producer writes the FP8 form
+ * directly).  C is formed exactly as fp8q_gemm forms it (acc as there),
+ * rounded to BF16 (nearest even) as with FP8Q_OUT_BF16, and that BF16 tensor
+ * is quantized per 1x128 tile along N exactly as fp8q_quantize_act
+ * (FP8Q_TILE_ROW, scale_mode) quantizes it: the result is bit for bit the
+ * unfused fp8q_gemm(FP8Q_OUT_BF16) followed by fp8q_quantize_act, without
+ * the BF16 round trip through HBM.
+ * a, a_scales, w, w_scales, M, N, K, acc as for fp8q_gemm; c_codes
+ * [M, ld_c >= N] E4M3; c_scales [M, ceil(N/128)] float32. */
+fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales,
+                                const uint8_t* w, const float* w_scales,
+                                int64_t M, int64_t N, int64_t K, int acc, int scale_mode,
+                                uint8_t* c_codes, int64_t ld_c, float* c_scales, hipStream_t stream);
+
 /* Grouped block-scaled GEMM for the MoE experts one device hosts
  * (jp-study.kr doc 258368 ¶1-¶2: activations quantized before the expert
  * dispatch; each device hosts several experts).  Rows

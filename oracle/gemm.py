@@ -24,6 +24,10 @@ the dequantized operands; the acceptance rule for a GPU result c is
     BF16 output:  c is the round-to-nearest-even BF16 of some float32 value
                   in [C - tol, C + tol], tol = 1e-5 * S + 1e-6  (an interval
                   test, since rounding is monotone)
+    E4M3 output (the BF16 output quantized per 1x128 tile along N, the
+                  producer-side answer to tmdrlife.com wr_id=13334 ¶1): each
+                  tile is the quantization of some BF16 tensor that passes
+                  the BF16 rule (``accept_quantized``)
 
 jp-study.kr doc 258368 ¶3 (Wgrad in FP8): the weight gradient is the same
 contraction over the token axis with both operands scaled per 128 tokens and
@@ -32,7 +36,9 @@ per row, dW[n, c] = sum_b sdy[n, b] * sx[c, b] * sum_{t in b} qdy[n, t] qx[c, t]
 Pins: tests/test_oracle_gemm.py (exact integer + Fraction brute force on the
 tiny-linear shape, constant-operand closed form, selector weights, zero
 scales, grouped == per-group dense, Wgrad == dense when scales are constant
-per block, the BF16 interval rule on hand-made cases).
+per block, the BF16 interval rule on hand-made cases, the quantized-output
+rule accepting the quantization of the exact result and rejecting planted
+code and scale errors).
 """
 
 import numpy as np
@@ -188,3 +194,59 @@ def accept_bf16(c_gpu_bf16_bits, c_ref, s_ref):
     v = (np.asarray(c_gpu_bf16_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
     v = v.astype(np.float64)
     return (v >= lo) & (v <= hi)
+
+
+def accept_quantized(codes_gpu, scales_gpu, c_ref, s_ref, mode):
+    """Quantized-output rule, per 1x128 tile along N (boolean [M, nb]): the
+    GPU tile must be the 1x128 quantization (oracle.quantize) of some BF16
+    tensor that passes ``accept_bf16`` elementwise.
+
+    Each element's admissible BF16 values form an interval [lo, hi]
+    (``accept_bf16``).  The tile's max-abs then lies between the largest of
+    the smallest admissible magnitudes and the largest of the largest ones;
+    the scale must be the scale of one BF16 value in that range, and each
+    code must lie between the codes of its interval's ends under that scale
+    (the quotient and the E4M3 rounding are monotone in the value).
+    """
+    from .e4m3 import decode, encode
+    from .quantize import TILE, _tile_scale
+
+    c_ref = np.asarray(c_ref, dtype=np.float64)
+    tol = tolerance(s_ref)
+    lo = _bf16_rne_value(_f32_toward(c_ref - tol, up=True))
+    hi = _bf16_rne_value(_f32_toward(c_ref + tol, up=False))
+    min_mag = np.where((lo <= 0) & (hi >= 0), 0.0, np.minimum(np.abs(lo), np.abs(hi)))
+    max_mag = np.maximum(np.abs(lo), np.abs(hi))
+    m, n = c_ref.shape
+    nb = -(-n // TILE)
+    codes_gpu = np.asarray(codes_gpu, dtype=np.uint8)[:, :n]
+    scales_gpu = np.asarray(scales_gpu, dtype=np.float32)
+    ok = np.zeros((m, nb), dtype=bool)
+    for b in range(nb):
+        sl = slice(b * TILE, min(n, (b + 1) * TILE))
+        a_lo = np.max(min_mag[:, sl], axis=1).astype(np.float32)
+        a_hi = np.max(max_mag[:, sl], axis=1).astype(np.float32)
+        s = scales_gpu[:, b]
+        # the BF16 values between a_lo and a_hi (both BF16 values >= 0) are
+        # consecutive bit patterns
+        b_lo = (a_lo.view(np.uint32) >> 16).astype(np.int64)
+        b_hi = (a_hi.view(np.uint32) >> 16).astype(np.int64)
+        span = b_hi - b_lo
+        s_ok = np.zeros(m, dtype=bool)
+        for k in range(int(min(span.max(initial=0), 64)) + 1):
+            bits = np.minimum(b_lo + k, b_hi).astype(np.uint32) << 16
+            s_ok |= _tile_scale(bits.view(np.float32), mode) == s
+        wide = span > 64  # degenerate tiles: the scale only has to be in range
+        s_ok |= wide & (s >= _tile_scale(a_lo, mode)) & (s <= _tile_scale(a_hi, mode))
+
+        def codes_of(v):
+            vf = v.astype(np.float32)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                q = vf / s[:, None]
+            return decode(encode(np.where(s[:, None] == 0, vf, q).astype(np.float32)))
+
+        d_lo, d_hi = codes_of(lo[:, sl]), codes_of(hi[:, sl])
+        got = decode(codes_gpu[:, sl])
+        c_ok = np.all((got >= np.minimum(d_lo, d_hi)) & (got <= np.maximum(d_lo, d_hi)), axis=1)
+        ok[:, b] = s_ok & c_ok
+    return ok

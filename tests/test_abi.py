@@ -115,6 +115,19 @@ def test_grouped_and_wgrad_validation(lib):
     assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
+def test_gemm_quantized_validation(lib):
+    f = lib.fp8q_gemm_quantized
+    # (a, sa, w, sw, M, N, K, acc, scale_mode, codes, ld_c, scales, stream)
+    assert f(P16, P16, P16, P16, 0, 4, 128, 0, 0, None, 4, None, None) == fp8q.OK
+    assert f(P16, P16, P16, P16, 4, 4, 128, 3, 0, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert f(P16, P16, P16, P16, 4, 4, 128, 0, 2, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG  # mode
+    assert f(P16, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None, None) == fp8q.ERR_INVALID_ARG  # scales
+    assert f(P16, P16, P16, P16, 4, 4, 100, 0, 0, P16, 4, P16, None) == fp8q.ERR_SHAPE  # K % 128
+    assert f(P16, P16, P16, P16, 4, 8, 128, 0, 0, P16, 4, P16, None) == fp8q.ERR_SHAPE  # ld_c < N
+    assert f(P16, P16, P16, P16, 4, 4, 128, 0, 0, P8, 4, P16, None) == fp8q.ERR_ALIGN
+    assert f(None, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG
+
+
 def test_gather_rows_validation(lib):
     g = lib.fp8q_gather_rows
     # (codes, rows, cols, ld_codes, scales, index, n_out, out, ld_out, out_scales, stream)
@@ -158,6 +171,7 @@ def test_valid_calls_reach_the_device_check(lib):
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 0, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_weight_t(P16, 4, 8, 8, 0, None, 0, None, P16, 16, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm_quantized(P16, P16, P16, P16, 4, 5, 128, 0, 1, P16, 5, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gather_rows(P16, 10, 64, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gather_rows(None, 0, 64, 64, None, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_swiglu_quantize(P16, 4, 100, 200, 0, P16, 100, P16, 1, None, 0, None, None) == fp8q.ERR_DEVICE

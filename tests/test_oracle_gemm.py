@@ -181,3 +181,35 @@ def test_acceptance_rule_f32_and_bf16():
     assert list(G.accept_bf16(bf([1.0, 1.0078125]), mid, np.zeros(2))) == [True, True]
     # 100 +- 0.01: the BF16 neighbours of 100 are 99.5 and 100.5 -> only 100
     assert list(G.accept_bf16(bf([100.0, 100.5, 99.5]), np.full(3, 100.0), np.full(3, 1000.0))) == [True, False, False]
+
+
+@pytest.mark.parametrize("mode", [Q.FREE, Q.POW2])
+def test_acceptance_rule_quantized_output(mode):
+    """The quantization of the exact result rounded to BF16 passes; a code
+    moved by one step where the tolerance cannot reach, or a doubled scale,
+    does not; so does the quantization of a BF16 result nudged within
+    tolerance."""
+    rng = np.random.default_rng(23)
+    a = synth.bf16_rne(rng.standard_normal((40, 256)).astype(np.float32))
+    w = synth.bf16_rne((rng.standard_normal((300, 256)) * 0.02).astype(np.float32))
+    ac, as_ = Q.quantize_rows(a)
+    wc, ws = Q.quantize_blocks(w)
+    c, s = G.gemm(ac, as_, wc, ws)
+    cb = e4m3.f32_to_bf16_bits_rne(c.astype(np.float32))
+    codes, scales = Q.quantize_rows(cb, mode)
+    ok = G.accept_quantized(codes, scales, c, s, mode)
+    assert ok.shape == (40, 3) and ok.all()
+    # a code two E4M3 steps away from the right one, on a large element
+    bad = codes.copy()
+    r, j = 5, int(np.argmax(np.abs(c[5, :128])))
+    bad[r, j] = (int(bad[r, j]) & 0x80) | ((int(bad[r, j]) & 0x7F) - 2)
+    acc = G.accept_quantized(bad, scales, c, s, mode)
+    assert not acc[r, 0] and acc.sum() == acc.size - 1
+    bad_s = scales.copy()
+    bad_s[7, 2] *= 2
+    assert not G.accept_quantized(codes, bad_s, c, s, mode)[7, 2]
+    # a BF16 result inside the tolerance (one float32 step away) quantizes to
+    # an accepted tile
+    nudged = np.nextafter(c.astype(np.float32), np.float32(np.inf))
+    codes2, scales2 = Q.quantize_rows(e4m3.f32_to_bf16_bits_rne(nudged), mode)
+    assert G.accept_quantized(codes2, scales2, c, s, mode).all()
