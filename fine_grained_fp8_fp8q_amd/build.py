@@ -61,7 +61,9 @@ def build(verbose=False):
         _run([cc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    # --no-undefined: a kernel whose host launch stub the compiler failed to
+    # emit shows up here instead of when the library is loaded
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

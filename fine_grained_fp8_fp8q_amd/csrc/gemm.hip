@@ -54,10 +54,18 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 512;
-constexpr int kATileBytes = BM * BK;                             // 32 KiB
-constexpr int kWTileBytes = BN * BK;                             // 32 KiB
-constexpr int kScaleOff = kATileBytes + kWTileBytes;             // A scales [256], W scales [256]
-constexpr int kStageBytes = kScaleOff + (BM + BN) * 4;           // 66 KiB
+// A stage holds one K block: the A rows of the tile (128 B each), the 256
+// W rows, then the A scales [256] and one W scale per column [256].  A full
+// tile's stage is 66 KiB (two stages); a grouped tile of at most 128 (64)
+// rows has a 16 (8) KiB A part, so three of its stages fit in 150 KiB.
+template <int AROWS>
+struct StageLayout {
+  static constexpr int kW = AROWS * BK;            // W rows start here
+  static constexpr int kS = kW + BN * BK;          // scales
+  static constexpr int kBytes = kS + (BM + BN) * 4;
+};
+constexpr int kFullStage = StageLayout<BM>::kBytes;     // 66 KiB
+constexpr int kSmallStage = StageLayout<128>::kBytes;   // 50 KiB (also holds the 64-row layout)
 
 enum Mode { kDense = 0, kGrouped = 1, kWgrad = 2 };
 // Output forms: float32, BF16 (RNE), or the BF16 value quantized per 1x128
@@ -168,30 +176,69 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
 }
 
 // One K block of the main loop.  `cur` (the stage multiplied now) and
-// `refill` (the stage the loads of block kb+1 go to) are distinct LDS
-// buffers; __restrict__ tells the compiler so, which lets it keep the refill
-// loads in flight across the LDS reads of `cur` instead of waiting for them.
-// The barrier is a bare s_barrier after an explicit vmcnt(0): every wave's
+// `refill` (the stage the loads of block kb+AHEAD go to) are distinct sets
+// of LDS arrays, so the compiler keeps those loads in flight across the LDS
+// reads of `cur` instead of waiting for them.  With AHEAD = 1 (two stages)
+// the barrier is a bare s_barrier after an explicit vmcnt(0): every wave's
 // loads of block kb have landed, and every LDS read of the stage being
 // refilled was consumed before its wave got here; __syncthreads() would add
-// nothing but a fence.  The asm memory clobber keeps the compiler from
+// nothing but a fence.  With AHEAD = 2 (three stages) the wait leaves the
+// newest refill in flight.  The asm memory clobber keeps the compiler from
 // moving LDS accesses across it.  Past the last block the refill re-reads
 // the last block (in bounds) into a stage that is never read again, so the
 // issue stays unconditional and the compiler's tracking of the loads in
 // flight stays exact.  `compute` calls refill_now() once, at the point where
 // the refill loads should go out.
-template <class Issue, class Compute>
+template <int AHEAD, int LOADS, class Issue, class Compute>
 __device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restrict__ cur,
                                          uint8_t* __restrict__ refill, Issue& issue, Compute& compute) {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  auto refill_now = [&]() { issue(min(kb + 1, nkb - 1), refill); };
+  if constexpr (AHEAD == 1) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    // the LOADS loads of block kb+1 (issued during block kb-1) may stay in
+    // flight; loads complete in order, so block kb's have landed
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+  }
+  auto refill_now = [&]() { issue(min(kb + AHEAD, nkb - 1), refill); };
   compute(cur, refill_now);
+}
+
+// The K loops.  Every stage is a __restrict__ parameter of the one function
+// that runs the whole loop: the compiler's tracking of loads in flight into
+// LDS tells stages apart only through that aliasing information, and it has
+// to hold between a stage's reads and the loads into the other stages issued
+// in earlier iterations.
+template <int LOADS, class Issue, class Compute>
+__device__ __forceinline__ void k_loop2(int nkb, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
+                                        Issue& issue, Compute& compute) {
+  if (nkb > 0) issue(0, s0);
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    run_step<1, LOADS>(kb, nkb, s0, s1, issue, compute);
+    run_step<1, LOADS>(kb + 1, nkb, s1, s0, issue, compute);
+  }
+  if (kb < nkb) run_step<1, LOADS>(kb, nkb, s0, s1, issue, compute);
+}
+
+template <int LOADS, class Issue, class Compute>
+__device__ __forceinline__ void k_loop3(int nkb, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
+                                        uint8_t* __restrict__ s2, Issue& issue, Compute& compute) {
+  if (nkb > 0) {
+    issue(0, s0);
+    issue(min(1, nkb - 1), s1);
+  }
+  for (int kb = 0; kb < nkb; kb += 3) {
+    run_step<2, LOADS>(kb, nkb, s0, s2, issue, compute);
+    if (kb + 1 < nkb) run_step<2, LOADS>(kb + 1, nkb, s1, s0, issue, compute);
+    if (kb + 2 < nkb) run_step<2, LOADS>(kb + 2, nkb, s2, s1, issue, compute);
+  }
 }
 
 template <int MODE, int OUT, int ACC>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[kStageBytes];
+  // two full stages, or (grouped tiles of at most 128 rows) three small ones
+  constexpr int kLdsBytes = MODE == kGrouped ? 3 * kSmallStage : 2 * kFullStage;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
   Tile t;
   if (!decode_tile<MODE>(g, t)) return;
@@ -209,24 +256,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   const int nkb = K / BK;
 
   // ---- global->LDS assignment: one wave instruction moves 8 rows x 128 B.
-  // Wave w moves rows 32w..32w+31 of both the A and the W tile.  Loads are
-  // buffer loads with an LDS destination.  Each buffer starts at the tile's
-  // first row and its size ends at the operand's last row, so rows past the
-  // operand read as zero (the hardware range check) instead of being
-  // clamped; A and W then share the per-lane row offsets.  The K-block
-  // offset goes in an SGPR, the LDS address in M0: issuing costs no VALU
-  // work.  Offsets fit in 32 bits (the host rejects operands of 2 GiB+).
+  // Full tiles: wave w moves rows 32w..32w+31 of both the A and the W tile
+  // (into the slot of its 128-row half).  Grouped tiles of at most 128 (64)
+  // rows move their A rows as 16 (8) rows per wave and the W tile as full
+  // tiles do.  Loads are buffer loads with an LDS destination.  The A buffer
+  // covers exactly the tile's rows and the W buffer ends at the operand's
+  // last row, so rows past either read as zero (the hardware range check,
+  // which also skips the memory access) instead of being clamped.  The
+  // K-block offset goes in an SGPR, the LDS address in M0: issuing costs no
+  // VALU work.  Offsets fit in 32 bits (the host rejects operands of 2 GiB+).
   const uint32_t rowb = (uint32_t)K;  // bytes per operand row
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.a + (size_t)t.m0 * rowb), 0, (int)((uint32_t)(g.rows - t.m0) * rowb), kRsrcFlags);
+      (void*)(g.a + (size_t)t.m0 * rowb), 0, (int)((uint32_t)(t.mend - t.m0) * rowb), kRsrcFlags);
   const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(t.w + (size_t)t.n0 * rowb), 0, (int)((uint32_t)(N - t.n0) * rowb), kRsrcFlags);
+  auto row_off = [&](int row) { return (uint32_t)row * rowb + 16u * (uint32_t)((lane & 7) ^ swz(row)); };
   uint32_t r_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 8 + (lane >> 3);
-    r_off[i] = (uint32_t)row * rowb + 16u * (uint32_t)((lane & 7) ^ swz(row));
-  }
+  for (int i = 0; i < 4; ++i) r_off[i] = row_off((wave * 4 + i) * 8 + (lane >> 3));
   // scales of the K block: waves 0-3 bring the A scales of rows 64w..64w+63,
   // waves 4-7 the W scale of columns 64(w-4)..+63 (one value per column, so
   // all modes share the LDS layout)
@@ -236,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   uint32_t s_off;
   if (wave < 4) {
     s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(g.sa + (size_t)t.m0 * nkb), 0,
-                                               (int)((uint32_t)(g.rows - t.m0) * sblk), kRsrcFlags);
+                                               (int)((uint32_t)(t.mend - t.m0) * sblk), kRsrcFlags);
     s_off = (uint32_t)sidx * sblk;
   } else if (MODE == kWgrad) {
     s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(t.sw + (size_t)t.n0 * nkb), 0,
@@ -247,16 +294,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
                                                (int)((uint32_t)((N - t.n0 + 127) >> 7) * sblk), kRsrcFlags);
     s_off = (uint32_t)(sidx >> 7) * sblk;
   }
-  const int s_dst = kScaleOff + (wave < 4 ? 0 : BM * 4) + (wave & 3) * 256;
+  const int s_dst = ((wave < 4 ? 0 : BM) + (wave & 3) * 64) * 4;  // bytes into the stage's scales
 
-  auto issue = [&](int kb, uint8_t* st) {
+  // full tile: 4 A + 4 W + 1 scale loads per wave
+  auto issue_full = [&](int kb, uint8_t* st) {
+    using L = StageLayout<BM>;
     const uint32_t kofs = (uint32_t)kb * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + kATileBytes + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + L::kW + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + s_dst), 4, s_off, (uint32_t)kb * 4u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + L::kS + s_dst), 4, s_off, (uint32_t)kb * 4u, 0, 0);
   };
 
   v4f acc[4][8];
@@ -268,6 +317,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   bool active = false;  // set per wave layout below
   const int r16 = lane & 15;
   const int c0 = 2 * (lane >> 4);
+  // a stage's layout for the wave layout of JN 16-column W fragments per
+  // wave (JN = 8: full tile; 4: at most 128 rows; 2: at most 64 rows)
+  auto layout_of = [](auto jn) {
+    constexpr int JN = decltype(jn)::value;
+    return StageLayout<JN == 8 ? BM : JN == 4 ? 128 : 64>{};
+  };
 
   // One K block: 8 W fragments (j) x 4 M fragments (f) x 4 K steps of 32 (q)
   // = 128 MFMAs per wave.  Explicit software pipeline, in program order:
@@ -289,14 +344,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     // Wgrad issues the refill later (see below); the other forms right away
     if (MODE != kWgrad || !active) refill_now();
     if (!active) return;
-    const float* S = reinterpret_cast<const float*>(st + kScaleOff);
-    const uint8_t* Ws = st + kATileBytes;
+    using L = decltype(layout_of(jn));
+    const float* S = reinterpret_cast<const float*>(st + L::kS);
     const int wrow0 = wn * WC + r16;
     const int wsw = swz(wrow0);  // same swizzle for rows wrow0 + 16j
     // one base address per half; fragment j is 2 KiB further (an
     // immediate offset of the LDS read)
-    const uint8_t* w_lo = Ws + wrow0 * 128 + 16 * (c0 ^ wsw);
-    const uint8_t* w_hi = Ws + wrow0 * 128 + 16 * ((c0 + 1) ^ wsw);
+    const uint8_t* Wb = st + L::kW + wrow0 * 128;
+    const uint8_t* w_lo = Wb + 16 * (c0 ^ wsw);
+    const uint8_t* w_hi = Wb + 16 * ((c0 + 1) ^ wsw);
     auto read_w_lo = [&](int j, v4i& lo) { lo = *reinterpret_cast<const v4i*>(w_lo + j * 2048); };
     auto read_w_hi = [&](int j, v4i& hi) { hi = *reinterpret_cast<const v4i*>(w_hi + j * 2048); };
     auto part = [](const v4i& lo, const v4i& hi, int q) {
@@ -420,9 +476,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       refill_now();
       return;
     }
-    const float* S = reinterpret_cast<const float*>(st + kScaleOff);
-    const uint8_t* Ws = st + kATileBytes;
+    using L = decltype(layout_of(jn));
+    const float* S = reinterpret_cast<const float*>(st + L::kS);
     const int wrow0 = wn * WC + r16;
+    const uint8_t* Wb = st + L::kW + wrow0 * 128;
+    const uint8_t* Ab = st + (wm * 64 + r16) * 128;
     const int wsw = swz(wrow0);
     const int arow0 = wm * 64 + r16;
     const int asw = swz(arow0);
@@ -432,10 +490,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     v8i wf[2];
-    wf[0] = read8(Ws + wrow0 * 128, wsw);
+    wf[0] = read8(Wb, wsw);
     v8i af[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) af[f] = read8(st + (arow0 + f * 16) * 128, asw);
+    for (int f = 0; f < 4; ++f) af[f] = read8(Ab + f * 16 * 128, asw);
     float sa[4], sc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
@@ -457,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     };
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
-      if (j < JN - 1) wf[(j + 1) & 1] = read8(Ws + (wrow0 + (j + 1) * 16) * 128, wsw);
+      if (j < JN - 1) wf[(j + 1) & 1] = read8(Wb + (j + 1) * 16 * 128, wsw);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         if (j > 0) fold(j - 1, f);
@@ -492,9 +550,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       refill_now();
       return;
     }
-    const float* S = reinterpret_cast<const float*>(st + kScaleOff);
-    const uint8_t* Ws = st + kATileBytes;
+    using L = decltype(layout_of(jn));
+    const float* S = reinterpret_cast<const float*>(st + L::kS);
     const int wrow0 = wn * WC + r16;
+    const uint8_t* Wb = st + L::kW + wrow0 * 128;
+    const uint8_t* Ab = st + (wm * 64 + r16) * 128;
     const int wsw = swz(wrow0);
     const int arow0 = wm * 64 + r16;
     const int asw = swz(arow0);
@@ -505,17 +565,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     };
     auto e8m0 = [](float x) { return (int)((__float_as_uint(x) >> 23) & 0xFFu); };
     v8i wf[2];
-    wf[0] = read8(Ws + wrow0 * 128, wsw);
+    wf[0] = read8(Wb, wsw);
     v8i af[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) af[f] = read8(st + (arow0 + f * 16) * 128, asw);
+    for (int f = 0; f < 4; ++f) af[f] = read8(Ab + f * 16 * 128, asw);
     int ae[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) ae[f] = e8m0(S[arow0 + f * 16]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
-      if (j < JN - 1) wf[(j + 1) & 1] = read8(Ws + (wrow0 + (j + 1) * 16) * 128, wsw);
+      if (j < JN - 1) wf[(j + 1) & 1] = read8(Wb + (j + 1) * 16 * 128, wsw);
       const int we = e8m0(S[BM + wrow0 + j * 16]);  // the scale of this lane's W row
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -544,18 +604,41 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     constexpr int JN = decltype(jn)::value;
     constexpr int WC = 16 * JN;
     active = (wm * 64 < t.mend - t.m0) && (wn * WC < N - t.n0);
-    // Two LDS stages: block kb+1 streams in while kb is multiplied.
-    if (nkb > 0) issue(0, stage0);
     auto comp = [&](const uint8_t* st, auto& refill_now) { compute(st, refill_now, jn); };
-    auto step = [&](int kb, const uint8_t* cur, uint8_t* refill) {
-      run_step(kb, nkb, cur, refill, issue, comp);
-    };
-    int kb = 0;
-    for (; kb + 2 <= nkb; kb += 2) {
-      step(kb, stage0, stage1);
-      step(kb + 1, stage1, stage0);
+    if constexpr (MODE == kGrouped && JN < 8) {
+      // A grouped tile of at most 128 (JN = 4) or 64 (JN = 2) rows does a
+      // fraction of a full tile's arithmetic per K block but streams the
+      // same 256 weight rows, so it is bound by the latency of its loads:
+      // three stages keep two K blocks in flight.  Its A rows are moved as
+      // 16 (8) rows per wave, the weight rows as in a full tile.
+      // (the A row offsets are spelled out instead of looping over a local
+      // constant inside the lambda: that form leaves the host compiler
+      // without the kernel's launch stub)
+      const uint32_t ra_off0 = row_off((JN == 4 ? wave * 2 : wave) * 8 + (lane >> 3));
+      const uint32_t ra_off1 = row_off((wave * 2 + 1) * 8 + (lane >> 3));
+      using L = decltype(layout_of(jn));
+      auto issue_small = [&](int kb, uint8_t* st) {
+        const uint32_t kofs = (uint32_t)kb * BK;
+        if constexpr (decltype(jn)::value == 4) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 2) * 1024), 16, ra_off0,
+                                                   kofs, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 2 + 1) * 1024), 16, ra_off1,
+                                                   kofs, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + wave * 1024), 16, ra_off0, kofs, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + L::kW + (wave * 4 + i) * 1024), 16,
+                                                   r_off[i], kofs, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + L::kS + s_dst), 4, s_off,
+                                                 (uint32_t)kb * 4u, 0, 0);
+      };
+      k_loop3<(JN == 4 ? 2 : 1) + 4 + 1>(nkb, lds, lds + kSmallStage, lds + 2 * kSmallStage, issue_small, comp);
+    } else {
+      // Two full stages: block kb+1 streams in while kb is multiplied.
+      k_loop2<9>(nkb, lds, lds + kFullStage, issue_full, comp);
     }
-    if (kb < nkb) step(kb, stage0, stage1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: lane holds C[m][n..n+3]
