@@ -13,6 +13,8 @@ Functions (names follow the C ABI without the ``fp8q_`` prefix):
 * ``quantize_act(x, tile_axis="row"|"token_t", scale_mode="free"|"pow2")``
   -> (codes uint8, scales float32)
 * ``quantize_weight(w, scale_mode="free"|"pow2")`` -> (codes, scales)
+* ``quantize_linear(x, w, act_scale_mode=..., weight_scale_mode=...)`` ->
+  (a_codes, a_scales, w_codes, w_scales) in one launch
 * ``gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16|torch.float32)``
 * ``grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=...)``
 * ``wgrad(dy_t, dy_scales, x_t, x_scales)``
@@ -35,7 +37,7 @@ OUT_F32, OUT_BF16 = 0, 1
 ACC_FP32, ACC_FP8_MFMA, ACC_FP8_MFMA_SCALED = 0, 1, 2
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
-SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_weight_t", "fp8q_gemm",
+SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_linear", "fp8q_quantize_weight_t", "fp8q_gemm",
            "fp8q_gemm_quantized", "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_gather_rows",
            "fp8q_swiglu_quantize",
            "fp8q_status_string")
@@ -61,6 +63,7 @@ def load_library(path=None):
     vp, i64, i32, ip = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     lib.fp8q_quantize_act.argtypes = [vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_weight.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp]
+    lib.fp8q_quantize_linear.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, i64, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_weight_t.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, vp, vp]
     lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_gemm_quantized.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
@@ -113,9 +116,11 @@ def _need(t, dtype, name):
 
 
 def _row_major(t, name):
-    if t.dim() != 2 or t.stride(1) != 1:
+    """Row stride of a 2-D tensor with contiguous rows (any stride is fine for
+    an empty one: nothing is read through it)."""
+    if t.dim() != 2 or (t.numel() and t.stride(1) != 1):
         raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
-    return t.stride(0)
+    return t.stride(0) if t.numel() else max(t.shape[1], 1)
 
 
 def _pad16(n):
@@ -173,6 +178,33 @@ def quantize_weight(w, scale_mode="free"):
                                              _stream(w))
     _check(st, "fp8q_quantize_weight")
     return codes, scales
+
+
+def quantize_linear(x, w, act_scale_mode="free", weight_scale_mode="free"):
+    """Both operands of a linear layer in one launch: the activation x
+    [M, K] per 1x128 tile and the weight w [N, K] per 128x128 block, bit for
+    bit ``quantize_act(x)`` and ``quantize_weight(w)``."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.bfloat16, "w")
+    ldx = _row_major(x, "x")
+    ldw = _row_major(w, "w")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("x and w must have the same K")
+    nb = (k + 127) // 128
+    ac = _alloc_codes(m, k, x.device)
+    as_ = torch.empty((m, nb), dtype=torch.float32, device=x.device)
+    wc = _alloc_codes(n, k, x.device)
+    ws = torch.empty(((n + 127) // 128, nb), dtype=torch.float32, device=x.device)
+    st = load_library().fp8q_quantize_linear(
+        _ptr(x), m, k, ldx if x.numel() else k, _scale_mode(act_scale_mode), _ptr(ac),
+        ac.stride(0) if ac.numel() else _pad16(max(k, 1)), _ptr(as_), _ptr(w), n, ldw if w.numel() else k,
+        _scale_mode(weight_scale_mode), _ptr(wc), wc.stride(0) if wc.numel() else _pad16(max(k, 1)), _ptr(ws),
+        _stream(x))
+    _check(st, "fp8q_quantize_linear")
+    return ac, as_, wc, ws
 
 
 def quantize_weight_t(w, scale_mode="free", both=True):

@@ -87,6 +87,30 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
                                             scale_mode == FP8Q_SCALE_POW2, codes, ld_codes, scales, stream));
 }
 
+fp8q_status fp8q_quantize_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ld_x, int act_scale_mode,
+                                 uint8_t* a_codes, int64_t ld_a, float* a_scales, const void* w_bf16, int64_t N,
+                                 int64_t ld_w, int weight_scale_mode, uint8_t* w_codes, int64_t ld_wc,
+                                 float* w_scales, hipStream_t stream) {
+  if (!dim_ok(M) || !dim_ok(K) || !dim_ok(N) || !dim_ok(ld_x) || !dim_ok(ld_a) || !dim_ok(ld_w) || !dim_ok(ld_wc))
+    return FP8Q_ERR_INVALID_ARG;
+  if (act_scale_mode != FP8Q_SCALE_FREE && act_scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (weight_scale_mode != FP8Q_SCALE_FREE && weight_scale_mode != FP8Q_SCALE_POW2) return FP8Q_ERR_INVALID_ARG;
+  if (K == 0 || (M == 0 && N == 0)) return FP8Q_OK;
+  if (M > 0 && (!x_bf16 || !a_codes || !a_scales)) return FP8Q_ERR_INVALID_ARG;
+  if (N > 0 && (!w_bf16 || !w_codes || !w_scales)) return FP8Q_ERR_INVALID_ARG;
+  if ((M > 0 && (ld_x < K || ld_a < K)) || (N > 0 && (ld_w < K || ld_wc < K))) return FP8Q_ERR_SHAPE;
+  const int64_t nb = (K + 127) / 128;
+  if (M * nb > kMaxDim || ((N + 127) / 128) * nb > kMaxDim || (M * nb + 63) / 64 + ((N + 127) / 128) * nb > kMaxDim)
+    return FP8Q_ERR_SHAPE;
+  if (M > 0 && (!aligned16(x_bf16) || !aligned16(a_codes) || !aligned16(a_scales))) return FP8Q_ERR_ALIGN;
+  if (N > 0 && (!aligned16(w_bf16) || !aligned16(w_codes) || !aligned16(w_scales))) return FP8Q_ERR_ALIGN;
+  if (fp8q_status st = check_device()) return st;
+  return launched(fp8q::launch_quant_linear(static_cast<const uint16_t*>(x_bf16), (int)M, (int)K, ld_x,
+                                            act_scale_mode == FP8Q_SCALE_POW2, a_codes, ld_a, a_scales,
+                                            static_cast<const uint16_t*>(w_bf16), (int)N, ld_w,
+                                            weight_scale_mode == FP8Q_SCALE_POW2, w_codes, ld_wc, w_scales, stream));
+}
+
 fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w, int scale_mode,
                                    uint8_t* codes, int64_t ld_codes, float* scales,
                                    uint8_t* codes_t, int64_t ld_codes_t, float* scales_t, hipStream_t stream) {

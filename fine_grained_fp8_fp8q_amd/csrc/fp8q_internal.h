@@ -16,6 +16,12 @@ hipError_t launch_quant_token_t(const uint16_t* x, int rows, int cols, int64_t l
 hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
                                uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream);
 
+// the activation x [m, k] in 1x128 tiles and the weight w [n, k] in 128x128
+// blocks, one launch
+hipError_t launch_quant_linear(const uint16_t* x, int m, int k, int64_t ldx, bool a_pow2, uint8_t* a_codes,
+                               int64_t lda, float* a_scales, const uint16_t* w, int n, int64_t ldw, bool w_pow2,
+                               uint8_t* w_codes, int64_t ldwc, float* w_scales, hipStream_t stream);
+
 hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
                                  uint8_t* codes, int64_t ldc, float* scales, uint8_t* codes_t,
                                  int64_t ldt, float* scales_t, hipStream_t stream);

@@ -17,15 +17,14 @@ namespace fp8q {
 // base + 4u + l/16, so every load instruction covers 4 consecutive tiles
 // (1 KiB when they share a row).
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int cols,
-                                                         int64_t ldx, uint8_t* __restrict__ codes,
-                                                         int64_t ldc, float* __restrict__ scales,
-                                                         int nb, int ntiles, bool vec) {
+__device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint16_t* __restrict__ x, int cols,
+                                                int64_t ldx, uint8_t* __restrict__ codes, int64_t ldc,
+                                                float* __restrict__ scales, int nb, int ntiles, bool vec) {
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int sub = lane & 15;
-  const int wave = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
-  const int nwaves = (int)(gridDim.x * 4u);
+  const int wave = (int)(((unsigned)bid * 256u + threadIdx.x) >> 6);
+  const int nwaves = nblocks * 4;
 
   for (int base = wave * 16; base < ntiles; base += nwaves * 16) {
     uint4 v[4];
@@ -61,22 +60,28 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   }
 }
 
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int cols,
+                                                         int64_t ldx, uint8_t* __restrict__ codes,
+                                                         int64_t ldc, float* __restrict__ scales,
+                                                         int nb, int ntiles, bool vec) {
+  quant_rows_body<POW2>((int)blockIdx.x, (int)gridDim.x, x, cols, ldx, codes, ldc, scales, nb, ntiles, vec);
+}
+
 // ------------------------------------------------------ 128x128 blocks ---
 // One workgroup (4 waves) per block.  Thread t holds rows t/16 + 16p
 // (p = 0..7) of the block, 8 BF16 each, so the block is read once and kept
 // in registers across the max-abs reduction.
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ w, int n,
-                                                           int k, int64_t ldw,
-                                                           uint8_t* __restrict__ codes, int64_t ldc,
-                                                           float* __restrict__ scales, int bk,
-                                                           bool vec) {
+__device__ __forceinline__ void quant_blocks_body(int bid, const uint16_t* __restrict__ w, int n, int k,
+                                                  int64_t ldw, uint8_t* __restrict__ codes, int64_t ldc,
+                                                  float* __restrict__ scales, int bk, bool vec) {
   __shared__ uint32_t red[4];
   const int tid = threadIdx.x;
   const int sub = tid & 15;
   const int r0 = tid >> 4;
-  const int bi = blockIdx.x / bk;
-  const int bj = blockIdx.x - bi * bk;
+  const int bi = bid / bk;
+  const int bj = bid - bi * bk;
   const int row0 = bi * 128, col0 = bj * 128 + sub * 8;
   const bool full = vec && (row0 + 128 <= n) && (bj * 128 + 128 <= k);
 
@@ -113,7 +118,36 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
       store8_masked(dst, c, k - col0);
     }
   }
-  if (tid == 0) scales[blockIdx.x] = ts.s;
+  if (tid == 0) scales[bid] = ts.s;
+}
+
+template <bool POW2>
+__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ w, int n,
+                                                           int k, int64_t ldw,
+                                                           uint8_t* __restrict__ codes, int64_t ldc,
+                                                           float* __restrict__ scales, int bk,
+                                                           bool vec) {
+  quant_blocks_body<POW2>((int)blockIdx.x, w, n, k, ldw, codes, ldc, scales, bk, vec);
+}
+
+// ------------------------------- both operands of a linear layer at once ---
+// The activation's 1x128 tiles (the first `ga` workgroups, as in
+// quant_rows_kernel) and the weight's 128x128 blocks (one workgroup each, as
+// in quant_blocks_kernel) in one launch: one grid ramp and drain instead of
+// two, and the two streams overlap.
+template <bool PA, bool PW>
+__global__ __launch_bounds__(256) void quant_linear_kernel(const uint16_t* __restrict__ x, int cols, int64_t ldx,
+                                                           uint8_t* __restrict__ a_codes, int64_t lda,
+                                                           float* __restrict__ a_scales, int nb, int ntiles,
+                                                           bool avec, int ga, const uint16_t* __restrict__ w,
+                                                           int n, int64_t ldw, uint8_t* __restrict__ w_codes,
+                                                           int64_t ldwc, float* __restrict__ w_scales, int bk,
+                                                           bool wvec) {
+  if ((int)blockIdx.x < ga) {
+    quant_rows_body<PA>((int)blockIdx.x, ga, x, cols, ldx, a_codes, lda, a_scales, nb, ntiles, avec);
+  } else {
+    quant_blocks_body<PW>((int)blockIdx.x - ga, w, n, cols, ldw, w_codes, ldwc, w_scales, bk, wvec);
+  }
 }
 
 // ---------------------------------- 128x128 blocks, plus the transpose ---
@@ -366,6 +400,29 @@ hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, boo
     hipLaunchKernelGGL(quant_blocks_kernel<true>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales, bk, vec);
   } else {
     hipLaunchKernelGGL(quant_blocks_kernel<false>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales, bk, vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_linear(const uint16_t* x, int m, int k, int64_t ldx, bool a_pow2, uint8_t* a_codes,
+                               int64_t lda, float* a_scales, const uint16_t* w, int n, int64_t ldw, bool w_pow2,
+                               uint8_t* w_codes, int64_t ldwc, float* w_scales, hipStream_t stream) {
+  const int nb = (k + 127) / 128;
+  const int ntiles = m * nb;
+  const int ga = m > 0 ? rows_grid(ntiles) : 0;
+  const int bn = (n + 127) / 128;
+  const int gw = n > 0 ? bn * nb : 0;
+  const bool avec = ldx % 8 == 0 && lda % 8 == 0;
+  const bool wvec = ldw % 8 == 0 && ldwc % 8 == 0;
+  const dim3 grid(ga + gw), block(256);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, x, k, ldx, a_codes, lda, a_scales, nb, ntiles, avec, ga, w,
+                       n, ldw, w_codes, ldwc, w_scales, nb, wvec);
+  };
+  if (a_pow2) {
+    if (w_pow2) go(quant_linear_kernel<true, true>); else go(quant_linear_kernel<true, false>);
+  } else {
+    if (w_pow2) go(quant_linear_kernel<false, true>); else go(quant_linear_kernel<false, false>);
   }
   return hipGetLastError();
 }

@@ -125,6 +125,19 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
                                  uint8_t* codes, int64_t ld_codes, float* scales,
                                  hipStream_t stream);
 
+/* Both operands of a linear layer in one launch: the activation x [M, K]
+ * exactly as fp8q_quantize_act(FP8Q_TILE_ROW, act_scale_mode) quantizes it
+ * (a_codes [M, ld_a >= K], a_scales [M, ceil(K/128)]) and the weight w [N, K]
+ * exactly as fp8q_quantize_weight(weight_scale_mode) quantizes it (w_codes
+ * [N, ld_wc >= K], w_scales [ceil(N/128), ceil(K/128)]) -- the online
+ * scaling of jp-study.kr doc 258368 ¶1 for the two inputs of one FP8 GEMM,
+ * with one grid ramp and drain instead of two.  M or N may be 0 (that
+ * operand is skipped; its pointers may then be NULL). */
+fp8q_status fp8q_quantize_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ld_x, int act_scale_mode,
+                                 uint8_t* a_codes, int64_t ld_a, float* a_scales,
+                                 const void* w_bf16, int64_t N, int64_t ld_w, int weight_scale_mode,
+                                 uint8_t* w_codes, int64_t ld_wc, float* w_scales, hipStream_t stream);
+
 /* The quantization of fp8q_quantize_weight, written for the activation
  * gradient too (jp-study.kr doc 258368 ¶3: Fprop, Dgrad and Wgrad all take
  * FP8 inputs).  dX[M,K] = dY[M,N] . W[N,K] reduces over N, so it needs W^T

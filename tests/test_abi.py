@@ -115,6 +115,23 @@ def test_grouped_and_wgrad_validation(lib):
     assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
+def test_quantize_linear_validation(lib):
+    f = lib.fp8q_quantize_linear
+    # (x, M, K, ld_x, amode, a_codes, ld_a, a_scales, w, N, ld_w, wmode, w_codes, ld_wc, w_scales, stream)
+    assert f(None, 0, 128, 128, 0, None, 128, None, None, 0, 128, 0, None, 128, None, None) == fp8q.OK
+    assert f(P16, 4, 0, 128, 0, P16, 128, P16, P16, 4, 128, 0, P16, 128, P16, None) == fp8q.OK
+    assert f(P16, 4, 128, 128, 2, P16, 128, P16, P16, 4, 128, 0, P16, 128, P16, None) == fp8q.ERR_INVALID_ARG
+    assert f(P16, 4, 128, 128, 0, P16, 128, P16, P16, 4, 128, 5, P16, 128, P16, None) == fp8q.ERR_INVALID_ARG
+    assert f(P16, 4, 128, 128, 0, None, 128, P16, P16, 4, 128, 0, P16, 128, P16, None) == fp8q.ERR_INVALID_ARG
+    assert f(P16, 4, 128, 128, 0, P16, 128, P16, P16, 4, 128, 0, P16, 128, None, None) == fp8q.ERR_INVALID_ARG
+    assert f(P16, 4, 128, 100, 0, P16, 128, P16, P16, 4, 128, 0, P16, 128, P16, None) == fp8q.ERR_SHAPE
+    assert f(P16, 4, 128, 128, 0, P16, 128, P16, P16, 4, 128, 0, P16, 127, P16, None) == fp8q.ERR_SHAPE
+    assert f(P8, 4, 128, 128, 0, P16, 128, P16, P16, 4, 128, 0, P16, 128, P16, None) == fp8q.ERR_ALIGN
+    assert f(P16, 4, 128, 128, 0, P16, 128, P16, P16, 4, 128, 0, P16, 128, P8, None) == fp8q.ERR_ALIGN
+    # one operand may be absent
+    assert f(None, 0, 128, 128, 0, None, 128, None, P8, 4, 128, 0, P16, 128, P16, None) == fp8q.ERR_ALIGN
+
+
 def test_gemm_quantized_validation(lib):
     f = lib.fp8q_gemm_quantized
     # (a, sa, w, sw, M, N, K, acc, scale_mode, codes, ld_c, scales, stream)
@@ -172,6 +189,10 @@ def test_valid_calls_reach_the_device_check(lib):
     assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_weight_t(P16, 4, 8, 8, 0, None, 0, None, P16, 16, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm_quantized(P16, P16, P16, P16, 4, 5, 128, 0, 1, P16, 5, P16, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_quantize_linear(P16, 4, 100, 100, 0, P16, 100, P16, P16, 5, 100, 1, P16, 100, P16,
+                                    None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_quantize_linear(None, 0, 128, 128, 0, None, 128, None, P16, 5, 128, 0, P16, 128, P16,
+                                    None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gather_rows(P16, 10, 64, 64, P16, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gather_rows(None, 0, 64, 64, None, P16, 5, P16, 64, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_swiglu_quantize(P16, 4, 100, 200, 0, P16, 100, P16, 1, None, 0, None, None) == fp8q.ERR_DEVICE

@@ -219,3 +219,35 @@ def test_deterministic():
     a = fp8q.quantize_act(x, "row", "free")
     b = fp8q.quantize_act(x, "row", "free")
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+_LINEAR_CASES = [(shape, modes) for shape in ((128, 256, 512), (70, 300, 200), (0, 130, 256), (33, 0, 384))
+                 for modes in (("free", "free"), ("pow2", "free"), ("free", "pow2"))] + [((4096, 4096, 7168),
+                                                                                        ("free", "free"))]
+
+
+@pytest.mark.parametrize("shape,modes", _LINEAR_CASES)
+def test_quantize_linear_equals_separate_calls(shape, modes):
+    """One launch for both operands of a linear layer: bit-identical to the
+    oracle's 1x128 and 128x128 quantizations (and so to the separate calls)."""
+    m, n, k = shape
+    am, wm = modes
+    rng = np.random.default_rng(m + 3 * n + k)
+    if (m, n, k) == (4096, 4096, 7168):
+        d = synth.dense_up()
+        x, w = d["a"], d["w"]
+    else:
+        x = synth.bf16_rne((rng.standard_normal((m, k)) * np.exp2(rng.integers(-4, 5, (m, 1)))).astype(np.float32))
+        w = synth.bf16_rne((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    say(f"[quant] quantize_linear M={m} N={n} K={k} {modes}")
+    ac, as_, wc, ws = fp8q.quantize_linear(dev_bf16(x), dev_bf16(w), act_scale_mode=am, weight_scale_mode=wm)
+    qa = Q.POW2 if am == "pow2" else Q.FREE
+    qw = Q.POW2 if wm == "pow2" else Q.FREE
+    if m:
+        want_c, want_s = Q.quantize_rows(x, qa)
+        assert_codes_equal(host_codes(ac), want_c, "activation codes")
+        assert_scales_equal(host(as_), want_s, "activation scales")
+    if n:
+        want_c, want_s = Q.quantize_blocks(w, qw)
+        assert_codes_equal(host_codes(wc), want_c, "weight codes")
+        assert_scales_equal(host(ws), want_s, "weight scales")
