@@ -15,7 +15,7 @@ Prints one JSON line:
   roofline   = the dominant kernel (the GEMM) against the dense FP8 MFMA peak
   cpu_baseline = the oracle timed on the host on a bounded sample
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 400] [--no-cpu-baseline]
 """
 
 import argparse
@@ -47,10 +47,11 @@ GEMM_TRAFFIC_BYTES = 212_760_000
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # the GPU needs a few milliseconds of load to reach its steady clock: the
-    # defaults keep the timed region (~25 ms) well past that ramp
-    p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=20)
+    # the GPU needs tens of milliseconds of load to reach its steady clock:
+    # the default warm-up (400 steps, ~90 ms, untimed) runs past that ramp,
+    # and the timed region is 200 steps (~45 ms)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (torch) --steps times; used to "
