@@ -30,13 +30,19 @@
 //
 // Data movement: both operands are K-contiguous (A [M,K], W [N,K]).  Each
 // 128-byte K slice of a row is moved global->LDS by buffer_load_dwordx4 with
-// an LDS destination (no VGPR staging), 8 rows per wave instruction, with the 16-byte chunks of
-// a row XOR-swizzled so the fragment reads (ds_read_b128, 16 rows at the
-// same chunk) hit distinct banks.  Lane group g (lanes 16g..16g+15) reads
-// bytes 32g..32g+31 of its row; the k order inside a block only has to be
-// the same for both operands.  Two LDS stages (66 KiB each): K block kb+1
-// streams in while kb is multiplied; one barrier per K block.  The per-row
-// scales of the K block ride along in the same stage.
+// an LDS destination (no VGPR staging), 8 rows per wave instruction, with
+// the 16-byte chunks of a row XOR-swizzled so the fragment reads
+// (ds_read_b128, 16 rows at the same chunk) hit distinct banks.  Lane group
+// g (lanes 16g..16g+15) reads bytes 32g..32g+31 of its row; the k order
+// inside a block only has to be the same for both operands.  Two LDS stages
+// (66 KiB each): K block kb+1 streams in while kb is multiplied; one barrier
+// per K block.  Grouped tiles of at most 128 rows use three smaller stages
+// (two K blocks in flight).  The per-row scales of the K block ride along in
+// the same stage.
+//
+// Output: float32, BF16 (nearest even), or -- dense only -- the BF16 value
+// quantized per 1x128 tile along N (E4M3 codes + float32 scales), the form a
+// following FP8 GEMM reads (tmdrlife.com wr_id=13334 ¶1).
 #include <type_traits>
 
 #include "fp8q_internal.h"
