@@ -471,6 +471,12 @@ def main():
 
     qa_us = kernel_us(q_act_i)
     qw_us = kernel_us(q_wgt_i)
+
+    def q_lin_i(i):
+        return lib.fp8q_quantize_linear(a_rot[i % ROT].data_ptr(), M, K, K, fp8q.SCALE_FREE,
+                                        ac_rot[i % ROT].data_ptr(), K, a_scales.data_ptr(), w_rot[i % ROT].data_ptr(),
+                                        N, K, fp8q.SCALE_FREE, wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
+    ql_us = kernel_us(q_lin_i)
     gemm_us = kernel_us(lambda i: gemm())
     gemm_f8_us = kernel_us(lambda i: lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
                                                    w_scales.data_ptr(), M, N, K, fp8q.OUT_BF16,
@@ -533,6 +539,11 @@ def main():
                                    "frac_hbm": round(qa_gbs / HBM_PEAK_GBS, 4), "bytes": ACT_BYTES},
             "quantize_weight_128x128": {"us": round(qw_us, 2), "GB/s": round(qw_gbs, 1),
                                         "frac_hbm": round(qw_gbs / HBM_PEAK_GBS, 4), "bytes": WGT_BYTES},
+            # both quantizers of the step in one launch (fp8q_quantize_linear)
+            "quantize_linear_act_and_weight": {
+                "us": round(ql_us, 2), "GB/s": round((ACT_BYTES + WGT_BYTES) / ql_us / 1e3, 1),
+                "frac_hbm": round((ACT_BYTES + WGT_BYTES) / ql_us / 1e3 / HBM_PEAK_GBS, 4),
+                "bytes": ACT_BYTES + WGT_BYTES},
             "gemm_block_scaled": {"us": round(gemm_us, 2), "TFLOP/s": round(gemm_tflops, 1),
                                   "frac_fp8_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
             # the same GEMM with its 128-element partials formed inside the

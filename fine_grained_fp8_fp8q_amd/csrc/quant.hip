@@ -219,7 +219,10 @@ __global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __r
   }
   // column j of the sub-block (byte j of every row's codes) goes to LDS as
   // row 8sb + j of the transposed block; the block then leaves as whole
-  // 128-byte W^T row segments (8 lanes per segment, 16 bytes each)
+  // 128-byte W^T row segments (8 lanes per segment, 16 bytes each).  The
+  // 16-byte chunks of a row are rotated by sb/2, so the 32 lanes of a
+  // half-wave write 64 distinct banks (unrotated, every second sb lands on
+  // the same two bank offsets).
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     uint32_t lo = 0, hi = 0;
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __r
       lo |= byte_of(j < 4 ? c[p].x : c[p].y, j & 3) << (8 * p);
       hi |= byte_of(j < 4 ? c[p + 4].x : c[p + 4].y, j & 3) << (8 * p);
     }
-    *reinterpret_cast<uint2*>(&tile_t[(8 * sb + j) * kTRowBytes + 8 * sa]) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(&tile_t[(8 * sb + j) * kTRowBytes + 8 * ((sa + 2 * (sb >> 1)) & 15)]) =
+        make_uint2(lo, hi);
   }
   __syncthreads();
   const int brow0 = bi * 128, bcol0 = bj * 128;
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __r
   for (int i = 0; i < 4; ++i) {
     const int q = tid + 256 * i;
     const int tr = q >> 3, ch = q & 7;   // transposed row (a column of W), 16-byte chunk
-    const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[tr * kTRowBytes + 16 * ch]);
+    const uint4 val = *reinterpret_cast<const uint4*>(&tile_t[tr * kTRowBytes + 16 * ((ch + (tr >> 4)) & 7)]);
     const int col = bcol0 + tr;
     uint8_t* dst = codes_t + (int64_t)col * ldt + brow0 + 16 * ch;
     if (full) {
@@ -258,7 +262,10 @@ __global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __r
 // so for each feature it holds four consecutive tokens: one code word.  The
 // per-feature max-abs runs over the 32 threads sharing c8; codes go through
 // LDS ([feature][token], 144-byte rows) and leave feature-major, 128 tokens
-// (one 128-byte line) per feature.
+// (one 128-byte line) per feature.  Within a row the token words are rotated
+// by 8 words per group of 8 features: the 64 lanes that write one word each
+// (8 feature groups x 8 token words) then hit 64 distinct banks, where the
+// unrotated rows put every feature group on the same two bank offsets.
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __restrict__ x, int rows,
                                                             int cols, int64_t ldx,
@@ -341,7 +348,8 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
       const uint32_t word = (j >> 1) == 0 ? v[p].x : (j >> 1) == 1 ? v[p].y : (j >> 1) == 2 ? v[p].z : v[p].w;
       e[p] = quotient<POW2>((j & 1) ? bf16_hi(word) : bf16_lo(word), ts);
     }
-    *reinterpret_cast<uint32_t*>(&tile[f * kRowBytes + 4 * q]) = pack4_e4m3(e[0], e[1], e[2], e[3]);
+    *reinterpret_cast<uint32_t*>(&tile[f * kRowBytes + 4 * ((q + 8 * c8) & 31)]) =
+        pack4_e4m3(e[0], e[1], e[2], e[3]);
   }
   __syncthreads();
 
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
   for (int it = 0; it < 2; ++it) {
     const int f = (tid >> 3) + 32 * it;
     const int ch = tid & 7;
-    const uint4 w = *reinterpret_cast<const uint4*>(&tile[f * kRowBytes + 16 * ch]);
+    const uint4 w = *reinterpret_cast<const uint4*>(&tile[f * kRowBytes + 16 * ((ch + 2 * (f >> 3)) & 7)]);
     uint8_t* dst = codes + (int64_t)(f0 + f) * ldc + t0 + 16 * ch;
     if (full) {
       st_stream16(dst, w);
