@@ -60,18 +60,27 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kThreads = 512;
-// A stage holds one K block: the A rows of the tile (128 B each), the 256
-// W rows, then the A scales [256] and one W scale per column [256].  A full
-// tile's stage is 66 KiB (two stages); a grouped tile of at most 128 (64)
-// rows has a 16 (8) KiB A part, so three of its stages fit in 150 KiB.
+// A stage holds one K block: the A rows of the tile (128 B each) and the
+// 256 W rows; a full tile's stage also holds the weight gradient's W scales
+// of the block, one per column [256].  A full tile's stage is 65 KiB (two
+// stages); a grouped tile of at most 128 (64) rows has a 16 (8) KiB A part,
+// so three of its stages fit in 144 KiB.
 template <int AROWS>
 struct StageLayout {
   static constexpr int kW = AROWS * BK;            // W rows start here
-  static constexpr int kS = kW + BN * BK;          // scales
-  static constexpr int kBytes = kS + (BM + BN) * 4;
+  static constexpr int kS = kW + BN * BK;          // weight-gradient W scales (full tiles)
+  static constexpr int kBytes = kS + (AROWS == BM ? BN * 4 : 0);
 };
-constexpr int kFullStage = StageLayout<BM>::kBytes;     // 66 KiB
-constexpr int kSmallStage = StageLayout<128>::kBytes;   // 50 KiB (also holds the 64-row layout)
+constexpr int kFullStage = StageLayout<BM>::kBytes;     // 65 KiB
+constexpr int kSmallStage = StageLayout<128>::kBytes;   // 48 KiB (also holds the 64-row layout)
+// The other scales live in their own double buffer after the stages: half
+// h holds one group of four K blocks, [256 A rows | 256 W columns] x 4
+// blocks (one W value per column: the scale of its 128-column block).  A
+// load that brings one block of 256 row scales touches 256 cache lines (the
+// scale rows are K/128 floats apart), against 512 for the block's operand
+// rows; a load of four blocks of 16 rows touches 16.
+constexpr int kSclHalf = (BM + BN) * 4 * 4;             // 8 KiB
+constexpr int kSclBytes = 2 * kSclHalf;
 
 enum Mode { kDense = 0, kGrouped = 1, kWgrad = 2 };
 // Output forms: float32, BF16 (RNE), or the BF16 value quantized per 1x128
@@ -194,57 +203,65 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
 // the last block (in bounds) into a stage that is never read again, so the
 // issue stays unconditional and the compiler's tracking of the loads in
 // flight stays exact.  `compute` calls refill_now() once, at the point where
-// the refill loads should go out.
+// the refill loads should go out, after its reads of the scale buffer `scl`
+// (the refill of step kb brings a quarter of the next group of four
+// blocks' scales into the other half).  A batch of loads starts with its
+// scale loads, so waiting for vmcnt(LOADS) (LOADS = the operand loads of
+// one batch) also covers batches that carry them.
 template <int AHEAD, int LOADS, class Issue, class Compute>
 __device__ __forceinline__ void run_step(int kb, int nkb, const uint8_t* __restrict__ cur,
-                                         uint8_t* __restrict__ refill, Issue& issue, Compute& compute) {
+                                         uint8_t* __restrict__ refill, uint8_t* __restrict__ scl, Issue& issue,
+                                         Compute& compute) {
   if constexpr (AHEAD == 1) {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
-    // the LOADS loads of block kb+1 (issued during block kb-1) may stay in
+    // the loads of block kb+1 (issued during block kb-1) may stay in
     // flight; loads complete in order, so block kb's have landed
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(LOADS) : "memory");
   }
-  auto refill_now = [&]() { issue(min(kb + AHEAD, nkb - 1), refill); };
-  compute(cur, refill_now);
+  auto refill_now = [&]() { issue(min(kb + AHEAD, nkb - 1), refill, scl, kb); };
+  compute(cur, scl, kb, refill_now);
 }
 
-// The K loops.  Every stage is a __restrict__ parameter of the one function
-// that runs the whole loop: the compiler's tracking of loads in flight into
-// LDS tells stages apart only through that aliasing information, and it has
-// to hold between a stage's reads and the loads into the other stages issued
-// in earlier iterations.
+// The K loops.  Every stage and the scale buffer are __restrict__
+// parameters of the one function that runs the whole loop: the compiler's
+// tracking of loads in flight into LDS tells them apart only through that
+// aliasing information, and it has to hold between a stage's reads and the
+// loads into the other stages issued in earlier iterations.
 template <int LOADS, class Issue, class Compute>
 __device__ __forceinline__ void k_loop2(int nkb, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
-                                        Issue& issue, Compute& compute) {
-  if (nkb > 0) issue(0, s0);
+                                        uint8_t* __restrict__ scl, Issue& issue, Compute& compute) {
+  if (nkb > 0) issue(0, s0, scl, -1);
   int kb = 0;
   for (; kb + 2 <= nkb; kb += 2) {
-    run_step<1, LOADS>(kb, nkb, s0, s1, issue, compute);
-    run_step<1, LOADS>(kb + 1, nkb, s1, s0, issue, compute);
+    run_step<1, LOADS>(kb, nkb, s0, s1, scl, issue, compute);
+    run_step<1, LOADS>(kb + 1, nkb, s1, s0, scl, issue, compute);
   }
-  if (kb < nkb) run_step<1, LOADS>(kb, nkb, s0, s1, issue, compute);
+  if (kb < nkb) run_step<1, LOADS>(kb, nkb, s0, s1, scl, issue, compute);
 }
 
 template <int LOADS, class Issue, class Compute>
 __device__ __forceinline__ void k_loop3(int nkb, uint8_t* __restrict__ s0, uint8_t* __restrict__ s1,
-                                        uint8_t* __restrict__ s2, Issue& issue, Compute& compute) {
+                                        uint8_t* __restrict__ s2, uint8_t* __restrict__ scl, Issue& issue,
+                                        Compute& compute) {
   if (nkb > 0) {
-    issue(0, s0);
-    issue(min(1, nkb - 1), s1);
+    issue(0, s0, scl, -1);
+    issue(min(1, nkb - 1), s1, scl, -2);
   }
   for (int kb = 0; kb < nkb; kb += 3) {
-    run_step<2, LOADS>(kb, nkb, s0, s2, issue, compute);
-    if (kb + 1 < nkb) run_step<2, LOADS>(kb + 1, nkb, s1, s0, issue, compute);
-    if (kb + 2 < nkb) run_step<2, LOADS>(kb + 2, nkb, s2, s1, issue, compute);
+    run_step<2, LOADS>(kb, nkb, s0, s2, scl, issue, compute);
+    if (kb + 1 < nkb) run_step<2, LOADS>(kb + 1, nkb, s1, s0, scl, issue, compute);
+    if (kb + 2 < nkb) run_step<2, LOADS>(kb + 2, nkb, s2, s1, scl, issue, compute);
   }
 }
 
 template <int MODE, int OUT, int ACC>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
-  // two full stages, or (grouped tiles of at most 128 rows) three small ones
-  constexpr int kLdsBytes = MODE == kGrouped ? 3 * kSmallStage : 2 * kFullStage;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  // two full stages, or (grouped tiles of at most 128 rows) three small
+  // ones, then the scale buffer
+  constexpr int kStageBytes = MODE == kGrouped ? 3 * kSmallStage : 2 * kFullStage;
+  static_assert(kStageBytes >= 2 * kFullStage, "full tiles of the grouped form use two full stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStageBytes + kSclBytes];
 
   Tile t;
   if (!decode_tile<MODE>(g, t)) return;
@@ -280,9 +297,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   uint32_t r_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) r_off[i] = row_off((wave * 4 + i) * 8 + (lane >> 3));
-  // scales of the K block: waves 0-3 bring the A scales of rows 64w..64w+63,
-  // waves 4-7 the W scale of columns 64(w-4)..+63 (one value per column, so
-  // all modes share the LDS layout)
+  // scales: waves 0-3 bring the A scales of rows 64w..64w+63, waves 4-7 the
+  // W scale of columns 64(w-4)..+63 (one value per column, so all forms
+  // share the layout)
   const uint32_t sblk = (uint32_t)nkb * 4u;  // bytes per scale row
   const int sidx = (wave & 3) * 64 + lane;
   __amdgpu_buffer_rsrc_t s_rsrc;
@@ -300,18 +317,51 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
                                                (int)((uint32_t)((N - t.n0 + 127) >> 7) * sblk), kRsrcFlags);
     s_off = (uint32_t)(sidx >> 7) * sblk;
   }
-  const int s_dst = ((wave < 4 ? 0 : BM) + (wave & 3) * 64) * 4;  // bytes into the stage's scales
+  // Scale buffer fill.  Waves 0-3 own A rows 64w..64w+63, waves 4-7 W
+  // columns 64(w-4)..+63, laid out [entry][4 blocks] in each half.  One
+  // 4-byte load instruction covers 16 entries x 4 blocks (lane i: entry i/4,
+  // block i%4), so the step kb refill brings quarter kb%4 of group kb/4+1
+  // into half (kb/4+1)%2, whose last reader (group kb/4-1) is behind the
+  // barrier of this step; group g is complete when step 4g begins.  The
+  // prologue (step -1) brings group 0 whole; step -2 (the second prologue
+  // batch of three stages) brings none.  Every offset is in the VGPR part, so
+  // the buffer's range check turns entries past the tile and blocks past
+  // k/128 into zeros.  The weight gradient's W scales (per column and block)
+  // go into the block's stage instead, one block per load.  Issued first in
+  // a batch.
+  const int q_entry = (wave & 3) * 64 + (lane >> 2);  // entry of quarter 0
+  const uint32_t q_row = MODE == kWgrad || wave < 4 ? (uint32_t)q_entry : (uint32_t)((wave & 3) >> 1);
+  const uint32_t q_voff = q_row * sblk + 4u * (uint32_t)(lane & 3);
+  auto scale_quarter = [&](uint8_t* scl, int grp, int qq) {
+    uint8_t* half = scl + (grp & 1) * kSclHalf + (wave < 4 ? 0 : BM * 16) + ((wave & 3) * 64 + 16 * qq) * 16;
+    const uint32_t rows = wave < 4 || MODE == kWgrad ? (uint32_t)(16 * qq) : 0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)half, 4, q_voff + rows * sblk + (uint32_t)grp * 16u,
+                                             0, 0, 0);
+  };
+  auto issue_scales = [&](int kb, uint8_t* st, uint8_t* scl, int step) {
+    if (MODE == kWgrad && wave >= 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + StageLayout<BM>::kS + (wave & 3) * 256), 4,
+                                               s_off, (uint32_t)kb * 4u, 0, 0);
+    } else if (step >= 0) {
+      scale_quarter(scl, (step >> 2) + 1, step & 3);
+    } else if (step == -1) {
+      scale_quarter(scl, 0, 0);
+      scale_quarter(scl, 0, 1);
+      scale_quarter(scl, 0, 2);
+      scale_quarter(scl, 0, 3);
+    }
+  };
 
-  // full tile: 4 A + 4 W + 1 scale loads per wave
-  auto issue_full = [&](int kb, uint8_t* st) {
+  // full tile: the scale load, then 4 A + 4 W loads per wave
+  auto issue_full = [&](int kb, uint8_t* st, uint8_t* scl, int step) {
     using L = StageLayout<BM>;
+    issue_scales(kb, st, scl, step);
     const uint32_t kofs = (uint32_t)kb * BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + L::kW + (wave * 4 + i) * 1024), 16, r_off[i], kofs, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + L::kS + s_dst), 4, s_off, (uint32_t)kb * 4u, 0, 0);
   };
 
   v4f acc[4][8];
@@ -344,14 +394,28 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   //     before the first MFMA of fragment j+1 that overwrites it, 4 MFMAs
   //     after its last one.
   // sched_barrier(0) keeps the compiler from regrouping the MFMAs.
-  auto compute_bf16 = [&](const uint8_t* st, auto& refill_now, auto jn) {
+  auto compute_bf16 = [&](const uint8_t* st, const float* SA, auto& refill_now, auto jn) {
     constexpr int JN = decltype(jn)::value;  // 16-column W fragments per wave
     constexpr int WC = 16 * JN;
-    // Wgrad issues the refill later (see below); the other forms right away
-    if (MODE != kWgrad || !active) refill_now();
-    if (!active) return;
+    if (!active) {
+      refill_now();
+      return;
+    }
     using L = decltype(layout_of(jn));
     const float* S = reinterpret_cast<const float*>(st + L::kS);
+    float sa[4];
+    const int arow0 = wm * 64 + r16;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sa[f] = SA[(arow0 + f * 16) * 4];
+    float sc[4];
+    if constexpr (MODE != kWgrad) {
+      const float swv = SA[(BM + wn * WC) * 4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
+    }
+    // Wgrad issues the refill later (see below); the other forms once the
+    // scales are read
+    if (MODE != kWgrad) refill_now();
     const int wrow0 = wn * WC + r16;
     const int wsw = swz(wrow0);  // same swizzle for rows wrow0 + 16j
     // one base address per half; fragment j is 2 KiB further (an
@@ -365,17 +429,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       const v4i& r = q < 2 ? lo : hi;
       return e4m3x8_to_bf16(r[(q & 1) * 2], r[(q & 1) * 2 + 1]);
     };
-    float sa[4];
-    const int arow0 = wm * 64 + r16;
     const int asw = swz(arow0);  // same swizzle for rows arow0 + 16f
-#pragma unroll
-    for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
-    float sc[4];
-    if constexpr (MODE != kWgrad) {
-      const float swv = S[BM + wn * WC];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
-    }
     // A fragments and W fragment 0 are widened q-part by q-part during
     // j = 0, each right before the MFMA group that first needs it, so the
     // block does not open with a burst of 80 converts and no MFMA (5%
@@ -414,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     // wave-uniform index the compiler keeps one register per fragment and
     // stage, which spilled).
     const int wn_lane = (tid >> 6) >> (wrows == 4 ? 2 : wrows == 2 ? 1 : 0);
-    const float* swp = S + BM + wn_lane * WC + 4 * (lane >> 4);
+    const float* swp = S + wn_lane * WC + 4 * (lane >> 4);
     v4f swj = v4f{0.f, 0.f, 0.f, 0.f};
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
@@ -475,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // Per K block: the fragments are read first (W fragment 0, then the four
   // A fragments, then the scales), the refill of the other stage goes out
   // after the first MFMA group, and W fragment j+1 is read while j runs.
-  auto compute_f8 = [&](const uint8_t* st, auto& refill_now, auto jn) {
+  auto compute_f8 = [&](const uint8_t* st, const float* SA, auto& refill_now, auto jn) {
     constexpr int JN = decltype(jn)::value;
     constexpr int WC = 16 * JN;
     if (!active) {
@@ -502,13 +556,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int f = 0; f < 4; ++f) af[f] = read8(Ab + f * 16 * 128, asw);
     float sa[4], sc[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sa[f] = S[arow0 + f * 16];
-    const float swv = S[BM + wn * WC];
+    for (int f = 0; f < 4; ++f) sa[f] = SA[(arow0 + f * 16) * 4];
+    const float swv = SA[(BM + wn * WC) * 4];
     __builtin_amdgcn_sched_barrier(0);
     v4f p[4];
     // Wgrad: column scales of the fragment being folded, read once per
     // fragment (after the previous fragment's folds) instead of per fold
-    const float* swp = S + BM + wn * WC + 4 * (lane >> 4);
+    const float* swp = S + wn * WC + 4 * (lane >> 4);
     v4f swj = v4f{0.f, 0.f, 0.f, 0.f};
     auto fold = [&](int j, int f) {
       if constexpr (MODE == kWgrad) {
@@ -549,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // into the same matrix-core accumulator -- the pages' "MMA with group
   // scaling" (tmdrlife.com wr_id=13334 ¶3) and, with it, no promotion: the
   // running sum never leaves the unit until the epilogue.
-  auto compute_f8s = [&](const uint8_t* st, auto& refill_now, auto jn) {
+  auto compute_f8s = [&](const uint8_t* st, const float* SA, auto& refill_now, auto jn) {
     constexpr int JN = decltype(jn)::value;
     constexpr int WC = 16 * JN;
     if (!active) {
@@ -557,7 +611,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       return;
     }
     using L = decltype(layout_of(jn));
-    const float* S = reinterpret_cast<const float*>(st + L::kS);
     const int wrow0 = wn * WC + r16;
     const uint8_t* Wb = st + L::kW + wrow0 * 128;
     const uint8_t* Ab = st + (wm * 64 + r16) * 128;
@@ -575,18 +628,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     v8i af[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) af[f] = read8(Ab + f * 16 * 128, asw);
-    int ae[4];
+    // every scale of the block is read before the refill goes out (it may
+    // write the other half of the scale buffer); the weight gradient's W
+    // scales (per column and block) are in the stage
+    const float* SS = reinterpret_cast<const float*>(st + L::kS);
+    int ae[4], we[JN];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) ae[f] = e8m0(S[arow0 + f * 16]);
+    for (int f = 0; f < 4; ++f) ae[f] = e8m0(SA[(arow0 + f * 16) * 4]);
+#pragma unroll
+    for (int j = 0; j < JN; ++j)  // this lane's W row
+      we[j] = e8m0(MODE == kWgrad ? SS[wrow0 + j * 16] : SA[(BM + wrow0 + j * 16) * 4]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < JN; ++j) {
       if (j < JN - 1) wf[(j + 1) & 1] = read8(Wb + (j + 1) * 16 * 128, wsw);
-      const int we = e8m0(S[BM + wrow0 + j * 16]);  // the scale of this lane's W row
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j & 1], af[f], acc[f][j], 0, 0,
-                                                                     0, we, 0, ae[f]);
+                                                                     0, we[j], 0, ae[f]);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (j == 0) {
@@ -596,13 +655,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     }
   };
 
-  auto compute = [&](const uint8_t* st, auto& refill_now, auto jn) {
+  auto compute = [&](const uint8_t* st, const uint8_t* scl, int kb, auto& refill_now, auto jn) {
+    // this block's scales in the scale buffer: A entry e at SA[4 e], W
+    // entry e at SA[4 (BM + e)]
+    const float* SA = reinterpret_cast<const float*>(scl + ((kb >> 2) & 1) * kSclHalf) + (kb & 3);
     if constexpr (ACC == 2) {
-      compute_f8s(st, refill_now, jn);
+      compute_f8s(st, SA, refill_now, jn);
     } else if constexpr (ACC == 1) {
-      compute_f8(st, refill_now, jn);
+      compute_f8(st, SA, refill_now, jn);
     } else {
-      compute_bf16(st, refill_now, jn);
+      compute_bf16(st, SA, refill_now, jn);
     }
   };
 
@@ -610,7 +672,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     constexpr int JN = decltype(jn)::value;
     constexpr int WC = 16 * JN;
     active = (wm * 64 < t.mend - t.m0) && (wn * WC < N - t.n0);
-    auto comp = [&](const uint8_t* st, auto& refill_now) { compute(st, refill_now, jn); };
+    auto comp = [&](const uint8_t* st, const uint8_t* scl, int kb, auto& refill_now) {
+      compute(st, scl, kb, refill_now, jn);
+    };
     if constexpr (MODE == kGrouped && JN < 8) {
       // A grouped tile of at most 128 (JN = 4) or 64 (JN = 2) rows does a
       // fraction of a full tile's arithmetic per K block but streams the
@@ -623,7 +687,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
       const uint32_t ra_off0 = row_off((JN == 4 ? wave * 2 : wave) * 8 + (lane >> 3));
       const uint32_t ra_off1 = row_off((wave * 2 + 1) * 8 + (lane >> 3));
       using L = decltype(layout_of(jn));
-      auto issue_small = [&](int kb, uint8_t* st) {
+      auto issue_small = [&](int kb, uint8_t* st, uint8_t* scl, int step) {
+        issue_scales(kb, st, scl, step);
         const uint32_t kofs = (uint32_t)kb * BK;
         if constexpr (decltype(jn)::value == 4) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_void_ptr)(st + (wave * 2) * 1024), 16, ra_off0,
@@ -637,13 +702,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
         for (int i = 0; i < 4; ++i)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_void_ptr)(st + L::kW + (wave * 4 + i) * 1024), 16,
                                                    r_off[i], kofs, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)(st + L::kS + s_dst), 4, s_off,
-                                                 (uint32_t)kb * 4u, 0, 0);
       };
-      k_loop3<(JN == 4 ? 2 : 1) + 4 + 1>(nkb, lds, lds + kSmallStage, lds + 2 * kSmallStage, issue_small, comp);
+      k_loop3<(JN == 4 ? 2 : 1) + 4>(nkb, lds, lds + kSmallStage, lds + 2 * kSmallStage, lds + kStageBytes,
+                                     issue_small, comp);
     } else {
       // Two full stages: block kb+1 streams in while kb is multiplied.
-      k_loop2<9>(nkb, lds, lds + kFullStage, issue_full, comp);
+      k_loop2<8>(nkb, lds, lds + kFullStage, lds + kStageBytes, issue_full, comp);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
