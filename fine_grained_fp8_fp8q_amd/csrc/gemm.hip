@@ -35,10 +35,11 @@
 // (ds_read_b128, 16 rows at the same chunk) hit distinct banks.  Lane group
 // g (lanes 16g..16g+15) reads bytes 32g..32g+31 of its row; the k order
 // inside a block only has to be the same for both operands.  Two LDS stages
-// (66 KiB each): K block kb+1 streams in while kb is multiplied; one barrier
+// (65 KiB each): K block kb+1 streams in while kb is multiplied; one barrier
 // per K block.  Grouped tiles of at most 128 rows use three smaller stages
-// (two K blocks in flight).  The per-row scales of the K block ride along in
-// the same stage.
+// (two K blocks in flight).  The row and column scales go through their own
+// double buffer, four K blocks at a time, a quarter of the next group with
+// every K block's refill.
 //
 // Output: float32, BF16 (nearest even), or -- dense only -- the BF16 value
 // quantized per 1x128 tile along N (E4M3 codes + float32 scales), the form a
