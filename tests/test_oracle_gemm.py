@@ -213,3 +213,24 @@ def test_acceptance_rule_quantized_output(mode):
     nudged = np.nextafter(c.astype(np.float32), np.float32(np.inf))
     codes2, scales2 = Q.quantize_rows(e4m3.f32_to_bf16_bits_rne(nudged), mode)
     assert G.accept_quantized(codes2, scales2, c, s, mode).all()
+
+
+def test_block_spread_inputs_expose_misplaced_scales():
+    """The scale-staging GPU cases (tests/test_gpu_scale_groups.py) feed tiles
+    and blocks whose magnitudes differ by up to 2^24: taking any one row's
+    scale from a neighbouring K block, a neighbouring row of the same 16-row
+    group, or the next group, moves outputs outside the tolerance."""
+    from tests.test_gpu_scale_groups import _block_spread, _tile_spread
+    rng = np.random.default_rng(106)
+    m, n, k = 64, 130, 128 * 6
+    a_c, a_s = Q.quantize_rows(_tile_spread(rng, m, k))
+    w_c, w_s = Q.quantize_blocks(_block_spread(rng, n, k))
+    ref, s = G.gemm(a_c, a_s, w_c, w_s)
+    def fails(a_s_bad, w_s_bad=w_s):
+        bad, _ = G.gemm(a_c, a_s_bad, w_c, w_s_bad)
+        return not G.accept_f32(bad, ref, s).all()
+    swap_block = a_s.copy(); swap_block[5, [1, 2]] = a_s[5, [2, 1]]    # blocks 1 and 2 of row 5
+    swap_group = a_s.copy(); swap_group[9, [3, 4]] = a_s[9, [4, 3]]    # last of group 0, first of group 1
+    swap_row = a_s.copy(); swap_row[[16, 17], 0] = a_s[[17, 16], 0]     # two rows of one 16-row quarter
+    swap_w = w_s.copy(); swap_w[1, [0, 4]] = w_s[1, [4, 0]]              # W block column 1, blocks 0 and 4
+    assert fails(swap_block) and fails(swap_group) and fails(swap_row) and fails(a_s, swap_w)
