@@ -121,10 +121,13 @@ def quantize_only_rates(torch, fp8q, lib, stream, reps):
         def fn(i):
             return lib.fp8q_quantize_act(xs[i & 1].data_ptr(), rows, cols, cols, fp8q.TILE_ROW, mode,
                                          cs[i & 1].data_ptr(), cols, ss.data_ptr(), stream.cuda_stream)
+        burst = _burst_us(torch, stream, fn)
         us = _event_us(torch, stream, fn, reps)
         out[f"act_16384x7168_{mode_name}"] = {"us": round(us, 2), "GB/s": round(abytes / us / 1e3, 1),
                                               "frac_hbm": round(abytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                                              "bytes": abytes}
+                                              "bytes": abytes, "us_first_20_after_idle": round(burst, 2),
+                                              "frac_hbm_first_20_after_idle":
+                                                  round(abytes / burst / 1e3 / HBM_PEAK_GBS, 4)}
     del xs, cs, ss
     wt = synth.quant_only_weight()
     n, k = wt.shape
@@ -137,9 +140,12 @@ def quantize_only_rates(torch, fp8q, lib, stream, reps):
     def fw(i):
         return lib.fp8q_quantize_weight(ws[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, cs[i & 1].data_ptr(),
                                         k, ss.data_ptr(), stream.cuda_stream)
+    burst = _burst_us(torch, stream, fw)
     us = _event_us(torch, stream, fw, reps)
     out["weight_7168x18432"] = {"us": round(us, 2), "GB/s": round(wbytes / us / 1e3, 1),
-                                "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wbytes}
+                                "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wbytes,
+                                "us_first_20_after_idle": round(burst, 2),
+                                "frac_hbm_first_20_after_idle": round(wbytes / burst / 1e3 / HBM_PEAK_GBS, 4)}
     return out
 
 
@@ -360,6 +366,16 @@ def dgrad_rates(torch, fp8q, lib, stream, reps, w):
                                  n, fp8q.OUT_BF16, acc, dx.data_ptr(), k, stream.cuda_stream)
         out[f"dgrad_{m}x{k}x{n}{acc_name}"] = _roofline(flop, nbytes, _event_us(torch, stream, fg, reps))
     return out
+
+
+def _burst_us(torch, stream, fn, reps=20):
+    """Average of `reps` launches started after 200 ms without GPU work.  The
+    HBM-bound kernels run at their full rate for the first ~1.5 ms of
+    sustained load and slower after that (the box's power management; the
+    sustained average is the figure the roofline fraction uses)."""
+    torch.cuda.synchronize()
+    time.sleep(0.2)
+    return _event_us(torch, stream, fn, reps)
 
 
 def _event_us(torch, stream, fn, reps):
