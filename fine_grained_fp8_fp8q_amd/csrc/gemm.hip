@@ -44,6 +44,7 @@
 // Output: float32, BF16 (nearest even), or -- dense only -- the BF16 value
 // quantized per 1x128 tile along N (E4M3 codes + float32 scales), the form a
 // following FP8 GEMM reads (tmdrlife.com wr_id=13334 ¶1).
+#include <atomic>
 #include <type_traits>
 
 #include "fp8q_internal.h"
@@ -104,6 +105,7 @@ struct GemmArgs {
   int rows;               // dense: M; grouped: rows_cap; wgrad: Nout
   int n, k, groups;
   int tiles_m, tiles_n;
+  int bn;                 // tile width in N: 256, or 224 for the weight gradient (see launch_wgrad)
 };
 
 // 16-byte chunk swizzle of a 128-byte LDS row: rows r and r+8 of a 16-row
@@ -184,7 +186,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
     t.m0 = tm * BM;
     t.mend = min(t.m0 + BM, g.rows);
     t.wrows = 4;
-    t.n0 = tn * BN;
+    t.n0 = tn * g.bn;
     t.w = g.w;
     t.sw = g.sw;
     return true;
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // wave (JN = 8: full tile; 4: at most 128 rows; 2: at most 64 rows)
   auto layout_of = [](auto jn) {
     constexpr int JN = decltype(jn)::value;
-    return StageLayout<JN == 8 ? BM : JN == 4 ? 128 : 64>{};
+    return StageLayout<JN >= 7 ? BM : JN == 4 ? 128 : 64>{};
   };
 
   // One K block: 8 W fragments (j) x 4 M fragments (f) x 4 K steps of 32 (q)
@@ -803,9 +805,34 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     } else {
       run(std::integral_constant<int, 2>{});
     }
+  } else if constexpr (MODE == kWgrad) {
+    // 224-column tiles: the waves split them as 2 x 112 columns (7 W
+    // fragments each); the stage still receives 256 W rows (the last 32
+    // belong to the next tile and are not used)
+    if (g.bn == 224) {
+      run(std::integral_constant<int, 7>{});
+    } else {
+      run(std::integral_constant<int, 8>{});
+    }
   } else {
     run(std::integral_constant<int, 8>{});
   }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    if (const int c = cache[dev].load(std::memory_order_relaxed)) return c;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <int MODE, int OUT>
@@ -830,6 +857,7 @@ hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
   g.tiles_m = (m + BM - 1) / BM;
   g.tiles_n = (n + BN - 1) / BN;
+  g.bn = BN;
   const int grid = g.tiles_m * g.tiles_n;
   return bf16_out ? launch_acc<kDense, kOutBF16>(g, grid, acc, stream)
                   : launch_acc<kDense, kOutF32>(g, grid, acc, stream);
@@ -843,6 +871,7 @@ hipError_t launch_gemm_quantized(const uint8_t* a, const float* a_scales, const 
   g.c = codes; g.ldc = ldc; g.cs = scales; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
   g.tiles_m = (m + BM - 1) / BM;
   g.tiles_n = (n + BN - 1) / BN;
+  g.bn = BN;
   const int grid = g.tiles_m * g.tiles_n;
   return pow2 ? launch_acc<kDense, kOutE4M3Pow2>(g, grid, acc, stream)
               : launch_acc<kDense, kOutE4M3>(g, grid, acc, stream);
@@ -857,6 +886,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a, const float* a_scales, const in
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = rows_cap; g.n = n; g.k = k; g.groups = groups;
   g.tiles_m = (rows_cap + BM - 1) / BM + groups;  // upper bound of m tiles over all groups
   g.tiles_n = (n + BN - 1) / BN;
+  g.bn = BN;
   const int grid = g.tiles_m * g.tiles_n;
   return bf16_out ? launch_acc<kGrouped, kOutBF16>(g, grid, acc, stream)
                   : launch_acc<kGrouped, kOutF32>(g, grid, acc, stream);
@@ -869,7 +899,17 @@ hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8
   g.a = dy_t; g.sa = dy_scales; g.w = x_t; g.sw = x_scales; g.offsets = nullptr;
   g.c = dw; g.ldc = lddw; g.vec_c = (lddw % 4) == 0; g.rows = nout; g.n = kin; g.k = t; g.groups = 1;
   g.tiles_m = (nout + BM - 1) / BM;
-  g.tiles_n = (kin + BN - 1) / BN;
+  // Tile width: one tile per CU and wave of tiles, so the time goes as
+  // (waves of tiles) x (tile width); 224 columns when that is smaller.  The
+  // 2048 x 7168 weight gradient has 224 tiles of 256 columns, which leave 32
+  // of 256 CUs idle, or 256 of 224, which fill them.
+  const int64_t cus = device_cus();
+  auto cost = [&](int bn) {
+    const int64_t tiles = (int64_t)g.tiles_m * ((kin + bn - 1) / bn);
+    return ((tiles + cus - 1) / cus) * bn;
+  };
+  g.bn = cost(224) < cost(BN) ? 224 : BN;
+  g.tiles_n = (kin + g.bn - 1) / g.bn;
   return launch_acc<kWgrad, kOutF32>(g, g.tiles_m * g.tiles_n, acc, stream);
 }
 

@@ -226,6 +226,22 @@ def test_wgrad_small_every_element(t, nout, kin):
     _accept(dw, ref, s, "wgrad small")
 
 
+def test_wgrad_tile_widths():
+    """The weight gradient picks 224-column tiles when that fills more CUs for
+    less time (most shapes here, and the 2048 x 7168 workload) and 256-column
+    tiles otherwise: 2048 x 8192 makes 256 tiles of 256 columns (one wave on
+    256 CUs) but 296 of 224.  Every element of that case."""
+    rng = np.random.default_rng(8192)
+    t, nout, kin = 256, 2048, 8192
+    dy = synth.bf16_rne(rng.standard_normal((t, nout)).astype(np.float32))
+    x = synth.bf16_rne(rng.standard_normal((t, kin)).astype(np.float32))
+    ops = _wgrad_operands(dy, x)
+    say(f"[gemm] wgrad T={t} {nout}x{kin} (256-column tiles)")
+    dw = fp8q.wgrad(*[dev(o) for o in ops])
+    ref, s = G.wgrad(*ops)
+    _accept(dw, ref, s, "wgrad 256-column tiles")
+
+
 def test_wgrad_full_sampled():
     d = synth.wgrad()
     ops = _wgrad_operands(d["dy"], d["x"])
