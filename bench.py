@@ -378,6 +378,39 @@ def _burst_us(torch, stream, fn, reps=20):
     return _event_us(torch, stream, fn, reps)
 
 
+def flushed_launch_us(torch, stream, fn, reps=20):
+    """Median and min of single launches, each after a 1 GiB buffer (more
+    than the 256 MB Infinity Cache and every L2) has been written, with one
+    HIP event pair per launch."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for i in range(reps):
+        scratch.fill_(i & 0xFF)
+        e0.record(stream)
+        if fn() != 0:
+            raise RuntimeError("fp8q call failed")
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    return float(np.median(times)), float(np.min(times))
+
+
+def rocm_smi_clocks():
+    """Current clocks reported by rocm-smi (read after the measurements), or
+    None where it is not available."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        text = r.stdout[r.stdout.index("{"):]
+        cards = json.loads(text)
+        card = cards[sorted(cards)[0]]
+        return {k.strip(" :"): v for k, v in card.items()}
+    except Exception:
+        return None
+
+
 def _event_us(torch, stream, fn, reps):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     fn(0)
@@ -520,6 +553,7 @@ def main():
                                            N, cqs.data_ptr(), sp)
     unfused_us = kernel_us(unfused)
     del cq, cqs
+    flush_med_us, flush_min_us = flushed_launch_us(torch, stream, gemm)
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     dg = dgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4), w)
     del a_rot, w_rot, ac_rot, wc_rot
@@ -573,6 +607,9 @@ def main():
                 "us": round(gemm_f8s_us, 2), "TFLOP/s": round(GEMM_FLOP / gemm_f8s_us / 1e6, 1),
                 "frac_fp8_mfma": round(GEMM_FLOP / gemm_f8s_us / 1e6 / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
         },
+        # single launches after a cache flush (the operands come from HBM)
+        "gemm_block_scaled_after_cache_flush": {"median_us": round(flush_med_us, 2), "min_us": round(flush_min_us, 2),
+                                                "launches": 20, "flush": "1 GiB written before each launch"},
         "gemm_quantized_output": {
             "workload": "4096x4096x7168 GEMM whose BF16 result is quantized 1x128 along N in the epilogue",
             "fused_us": round(gemm_q_us, 2), "fused_TFLOP/s": round(GEMM_FLOP / gemm_q_us / 1e6, 1),
@@ -587,6 +624,7 @@ def main():
                      "traffic": GEMM_TRAFFIC_BYTES},
         "cpu_baseline": None,
     }
+    out["rocm_smi_clocks_after_run"] = rocm_smi_clocks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
