@@ -60,3 +60,31 @@ def assert_scales_equal(got, want, what):
     assert g.shape == w.shape, (what, g.shape, w.shape)
     bad = np.argwhere(g != w)
     assert bad.size == 0, f"{what}: {len(bad)} scale mismatches, first at {tuple(bad[0])}: got {g[tuple(bad[0])]:#010x} want {w[tuple(bad[0])]:#010x}"
+
+
+_MOE_CACHE = {}
+
+
+def moe_operands():
+    """The MoE workload (8192 tokens, top-8 over 256 experts, 16 hosted) as
+    the oracle quantizes it (free scales): the gathered 1x128 codes and scales
+    of the up-projection input, those of the down-projection input, and every
+    hosted expert's 128x128 weight codes and scales.  Computed once per
+    process (the weight quantization alone takes about a minute on the host);
+    the BF16 weights are not kept."""
+    if "ops" not in _MOE_CACHE:
+        import synth
+        from oracle import quantize as Q
+        d = synth.moe_grouped(tokens=8192, hidden=7168, inter=2048)
+        x_c, x_s = Q.quantize_rows(d["x"])
+        h_c, h_s = Q.quantize_rows(d["h"])
+
+        def blocks(w):
+            q = [Q.quantize_blocks(w[i]) for i in range(w.shape[0])]
+            return np.stack([c for c, _ in q]), np.stack([s for _, s in q])
+
+        up = (x_c[d["gather"]], x_s[d["gather"]]) + blocks(d["w_up"])
+        down = (h_c, h_s) + blocks(d["w_down"])
+        meta = {k: d[k] for k in ("offsets", "counts", "gather")}
+        _MOE_CACHE["ops"] = (meta, {"up": up, "down": down})
+    return _MOE_CACHE["ops"]

@@ -20,7 +20,7 @@ import torch
 import fine_grained_fp8_fp8q_amd as fp8q
 from oracle import e4m3, gemm as G, quantize as Q
 import synth
-from tests.gpu_util import dev, dev_bf16, host, host_bf16_bits, need_gpu, say
+from tests.gpu_util import dev, dev_bf16, host, host_bf16_bits, moe_operands, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -177,10 +177,10 @@ def test_grouped_small_every_element(out_dtype):
 
 
 def test_grouped_moe_one_gpu_share_sampled():
-    d, cases = _grouped_case(tokens=8192, hidden=7168, inter=2048, with_down=True)
+    d, cases = moe_operands()
     offs = d["offsets"]
     say(f"[gemm] MoE grouped 16 experts, M per expert {d['counts'].tolist()}")
-    for name, (a_c, a_s, wc, ws) in zip(("up", "down"), cases):
+    for name, (a_c, a_s, wc, ws) in cases.items():
         c = fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out_dtype=torch.bfloat16)
         cb = host_bf16_bits(c)
         rng = np.random.default_rng(2)

@@ -22,7 +22,7 @@ import torch
 import fine_grained_fp8_fp8q_amd as fp8q
 import synth
 from oracle import accum, e4m3, gemm as G, quantize as Q
-from tests.gpu_util import dev, host, host_bf16_bits, need_gpu, say
+from tests.gpu_util import dev, host, host_bf16_bits, moe_operands, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +165,29 @@ def test_native_grouped_small_every_element():
         rows, cols = _all_pairs(hi - lo, wc.shape[1])
         ref, s, t = accum.gemm_at_mfma(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rows, cols)
         _accept_model(torch.from_numpy(got[lo:hi]), ref, s, t, f"grouped expert {gi}")
+
+
+def test_native_grouped_moe_one_gpu_share_sampled():
+    """The MoE workload (8192 tokens, top-8 over 256 experts, 16 hosted) in
+    the FP8-unit form: up 7168 -> 4096 and down 2048 -> 7168, 300 random
+    outputs plus the corners of every hosted expert, against the unit
+    model."""
+    d, cases = moe_operands()
+    offs = d["offsets"]
+    rng = np.random.default_rng(11)
+    for name, (a_c, a_s, wc, ws) in cases.items():
+        say(f"[native] MoE grouped {name}, M per expert {d['counts'].tolist()}")
+        c = fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out_dtype=torch.float32, acc=ACC)
+        n = wc.shape[1]
+        for gi in range(len(offs) - 1):
+            lo, hi = int(offs[gi]), int(offs[gi + 1])
+            if hi == lo:
+                continue
+            rows = np.concatenate([rng.integers(0, hi - lo, 300), [0, 0, hi - lo - 1, hi - lo - 1]])
+            cols = np.concatenate([rng.integers(0, n, 300), [0, n - 1, 0, n - 1]])
+            got = c[torch.from_numpy(rows + lo).cuda(), torch.from_numpy(cols).cuda()]
+            ref, s, t = accum.gemm_at_mfma(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rows, cols)
+            _accept_model(got, ref, s, t, f"MoE {name} expert {gi}")
 
 
 def test_native_grouped_equals_dense_per_group():
