@@ -226,20 +226,31 @@ def test_wgrad_small_every_element(t, nout, kin):
     _accept(dw, ref, s, "wgrad small")
 
 
-def test_wgrad_tile_widths():
+@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma"])
+def test_wgrad_tile_widths(acc):
     """The weight gradient picks 224-column tiles when that fills more CUs for
     less time (most shapes here, and the 2048 x 7168 workload) and 256-column
     tiles otherwise: 2048 x 8192 makes 256 tiles of 256 columns (one wave on
-    256 CUs) but 296 of 224.  Every element of that case."""
+    256 CUs) but 296 of 224.  Every element of that case (FP32-grade), or a
+    sample covering every row and column (FP8 unit, against the unit model)."""
+    from oracle import accum
+    from tests.test_gpu_native import _accept_model
     rng = np.random.default_rng(8192)
     t, nout, kin = 256, 2048, 8192
     dy = synth.bf16_rne(rng.standard_normal((t, nout)).astype(np.float32))
     x = synth.bf16_rne(rng.standard_normal((t, kin)).astype(np.float32))
     ops = _wgrad_operands(dy, x)
-    say(f"[gemm] wgrad T={t} {nout}x{kin} (256-column tiles)")
-    dw = fp8q.wgrad(*[dev(o) for o in ops])
-    ref, s = G.wgrad(*ops)
-    _accept(dw, ref, s, "wgrad 256-column tiles")
+    say(f"[gemm] wgrad T={t} {nout}x{kin} (256-column tiles) acc={acc}")
+    dw = fp8q.wgrad(*[dev(o) for o in ops], acc=acc)
+    if acc == "fp32":
+        ref, s = G.wgrad(*ops)
+        _accept(dw, ref, s, "wgrad 256-column tiles")
+        return
+    rows = np.concatenate([np.arange(nout), rng.integers(0, nout, kin), rng.integers(0, nout, 3000)])
+    cols = np.concatenate([rng.integers(0, kin, nout), np.arange(kin), rng.integers(0, kin, 3000)])
+    got = dw[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()]
+    ref, s, tt = accum.gemm_at_mfma(ops[0], ops[1], ops[2], ops[3], rows, cols, w_block_rows=False)
+    _accept_model(got, ref, s, tt, "wgrad 256-column tiles, FP8 unit")
 
 
 def test_wgrad_full_sampled():
