@@ -20,7 +20,7 @@ import torch
 import fine_grained_fp8_fp8q_amd as fp8q
 from oracle import e4m3, gemm as G, quantize as Q
 import synth
-from tests.gpu_util import dev, dev_bf16, host, host_bf16_bits, moe_operands, need_gpu, say
+from tests.gpu_util import dev, host, host_bf16_bits, moe_operands, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
