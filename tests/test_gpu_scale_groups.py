@@ -84,14 +84,17 @@ def test_dense_scale_groups(nkb, acc):
                         f"dense scaled k/128={nkb}")
 
 
+@pytest.mark.parametrize("n", [256, 328])
 @pytest.mark.parametrize("acc", ["fp32", "fp8_mfma"])
-def test_grouped_scale_groups(acc):
-    # four experts of 0, 70, 300 and 129 rows (tiles of every wave layout)
+def test_grouped_scale_groups(acc, n):
+    # four experts of 0, 70, 300 and 129 rows (tiles of every wave layout),
+    # N a multiple of the tile width or not (a last N tile of 72 columns,
+    # with a partial W block)
     counts = np.array([0, 70, 300, 129])
     offs = np.zeros(len(counts) + 1, np.int32)
     offs[1:] = np.cumsum(counts)
-    rows, n, k = int(offs[-1]), 256, 128 * 7
-    rng = np.random.default_rng(7)
+    rows, k = int(offs[-1]), 128 * 7
+    rng = np.random.default_rng(7 + n)
     a_c, a_s = Q.quantize_rows(_tile_spread(rng, rows, k))
     q = [Q.quantize_blocks(_block_spread(rng, n, k)) for _ in counts]
     wc, ws = np.stack([c for c, _ in q]), np.stack([s for _, s in q])
@@ -99,7 +102,7 @@ def test_grouped_scale_groups(acc):
     c = fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out_dtype=torch.float32, acc=acc)
     if acc == "fp32":
         ref, s = G.grouped_gemm(a_c, a_s, offs, wc, ws)
-        _accept(c, ref, s, "grouped k/128=7")
+        _accept(c, ref, s, f"grouped k/128=7 N={n}")
         return
     for gi in range(len(counts)):
         lo, hi = int(offs[gi]), int(offs[gi + 1])
@@ -108,7 +111,7 @@ def test_grouped_scale_groups(acc):
         rr, cc = _sample(rng, hi - lo, n)
         got = c[torch.from_numpy(rr + lo).cuda(), torch.from_numpy(cc).cuda()]
         ref, s, t = accum.gemm_at_mfma(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rr, cc)
-        _accept_model(got, ref, s, t, f"grouped fp8 unit expert {gi}")
+        _accept_model(got, ref, s, t, f"grouped fp8 unit N={n} expert {gi}")
 
 
 @pytest.mark.parametrize("nkb", [7, 9])
