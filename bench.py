@@ -371,7 +371,7 @@ def dgrad_rates(torch, fp8q, lib, stream, reps, w):
 def _burst_us(torch, stream, fn, reps=20):
     """Average of `reps` launches started after 200 ms without GPU work.  The
     HBM-bound kernels run at their full rate for the first ~1.5 ms of
-    sustained load and slower after that (the box's power management; the
+    sustained load and slower after that (the GPU's power management; the
     sustained average is the figure the roofline fraction uses)."""
     torch.cuda.synchronize()
     time.sleep(0.2)
@@ -430,7 +430,7 @@ def main():
         copy_calibration(args.steps)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "fp8q runs on one GPU only (no multi-GPU path); --gpus must be 1"}))
         sys.exit(2)
 
     import torch

@@ -13,10 +13,10 @@ accumulator aligned to the running maximum exponent (W=None: a float32
 accumulator); at the end of each interval the partial is added to a float32
 register ("promotion").  interval = len(terms) means no promotion.
 
-Readings (the design doc lists them): the alignment truncates toward zero, both
-the accumulator and the incoming product are put on the grid 2^(E-W+1) of the
-larger exponent E before the exact addition; products enter as float64
-values of the dequantized operands.  The float32 steps are emulated through
+Readings taken where the pages are silent: the alignment truncates toward
+zero, both the accumulator and the incoming product are put on the grid
+2^(E-W+1) of the larger exponent E before the exact addition; products enter
+as float64 values of the dequantized operands.  The float32 steps are emulated through
 float64 followed by a float32 cast.
 
 Parity: pinned only in its closed-form special cases (W large equals the

@@ -11,7 +11,7 @@ infrastructure.
   pass.  The down-projection's FP8 input is the 1x128 quantization of the
   SwiGLU output.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * SwiGLU(g, u) = silu(g) * u with silu(g) = g / (1 + e^-g); the up-projection
   output holds the gate in its first half of columns and the up values in

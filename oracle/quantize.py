@@ -7,7 +7,7 @@ wr_id=40936 ¶3: for some activations (inputs of the Linear after attention,
 SwiGLU inputs in MoE, the activation gradient before MoE down-projections)
 the scaling factors are integral powers of 2.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * free scale  s = RN32(amax / 448): the max-abs element lands on the largest
   E4M3 magnitude; the code of x is E4M3_RNE(RN32(x / s)), an IEEE float32
