@@ -13,6 +13,8 @@ Prints one JSON line:
   kernels    = per-kernel average durations from HIP events on the launch
                stream around --steps back-to-back launches of that kernel,
                with GB/s or TFLOP/s and the fraction of the MI355X roofline
+  *_after_cache_flush = the step's GEMM and quantizer as single launches,
+               each after a 1 GiB write that evicts the caches (median, min)
   roofline   = the dominant kernel (the GEMM) against the dense FP8 MFMA peak
   cpu_baseline = the oracle timed on the host on a bounded sample
 
@@ -554,6 +556,7 @@ def main():
     unfused_us = kernel_us(unfused)
     del cq, cqs
     flush_med_us, flush_min_us = flushed_launch_us(torch, stream, gemm)
+    qflush_med_us, qflush_min_us = flushed_launch_us(torch, stream, lambda: q_lin_i(0))
     quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
     dg = dgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4), w)
     del a_rot, w_rot, ac_rot, wc_rot
@@ -610,6 +613,10 @@ def main():
         # single launches after a cache flush (the operands come from HBM)
         "gemm_block_scaled_after_cache_flush": {"median_us": round(flush_med_us, 2), "min_us": round(flush_min_us, 2),
                                                 "launches": 20, "flush": "1 GiB written before each launch"},
+        "quantize_linear_after_cache_flush": {
+            "median_us": round(qflush_med_us, 2), "min_us": round(qflush_min_us, 2),
+            "frac_hbm_median": round((ACT_BYTES + WGT_BYTES) / qflush_med_us / 1e3 / HBM_PEAK_GBS, 4),
+            "launches": 20, "flush": "1 GiB written before each launch"},
         "gemm_quantized_output": {
             "workload": "4096x4096x7168 GEMM whose BF16 result is quantized 1x128 along N in the epilogue",
             "fused_us": round(gemm_q_us, 2), "fused_TFLOP/s": round(GEMM_FLOP / gemm_q_us / 1e6, 1),
