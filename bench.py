@@ -401,10 +401,19 @@ def flushed_launch_us(torch, stream, fn, reps=20):
 
 def rocm_smi_clocks():
     """Current clocks reported by rocm-smi (read after the measurements), or
-    None where it is not available."""
+    None where it is not available.  rocm-smi is a Python script: it is run
+    by this interpreter as a child process, not through its `env` shebang,
+    so no process that has loaded a profiler's GPU library replaces itself
+    with another program."""
+    import shutil
     import subprocess
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        smi = shutil.which("rocm-smi")
+        if smi is None:
+            return None
+        target = os.path.realpath(smi)
+        cmd = [sys.executable, target] if target.endswith(".py") else [smi]
+        r = subprocess.run(cmd + ["--showclocks", "--json"], capture_output=True, text=True, timeout=30)
         text = r.stdout[r.stdout.index("{"):]
         cards = json.loads(text)
         card = cards[sorted(cards)[0]]
