@@ -63,7 +63,7 @@ fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, in
   const int64_t code_row = tile_axis == FP8Q_TILE_ROW ? cols : rows;
   if (ld_codes < code_row) return FP8Q_ERR_SHAPE;
   const int64_t tiles = tile_axis == FP8Q_TILE_ROW ? rows * ((cols + 127) / 128) : cols * ((rows + 127) / 128);
-  if (tiles > kMaxDim || (tile_axis == FP8Q_TILE_TOKEN_T && (cols + 63) / 64 > 65535)) return FP8Q_ERR_SHAPE;
+  if (tiles > kMaxDim) return FP8Q_ERR_SHAPE;  // also bounds the token-axis grid (tiles / 64 + blocks)
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
   const bool pow2 = scale_mode == FP8Q_SCALE_POW2;

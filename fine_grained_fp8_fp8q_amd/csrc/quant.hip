@@ -256,8 +256,21 @@ __global__ __launch_bounds__(256) void quant_blocks_t_kernel(const uint16_t* __r
   }
 }
 
+// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8).
+// This maps them so that each XCD runs one contiguous range of logical
+// blocks: the token blocks of a feature group follow one another on one XCD,
+// and the 4-byte scales they write, adjacent in each feature's scale row,
+// meet in that XCD's L2 as whole lines instead of reaching memory as
+// partial-line writes from eight L2s.
+__device__ __forceinline__ int xcd_block(int bid, int nblk) {
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return xcd * per + min(xcd, rem) + idx;
+}
+
 // --------------------------------------------- 128x1 token-axis tiles ---
-// Workgroup tile: 128 tokens (rows of x) x 64 features (columns of x).
+// Workgroup tile: 128 tokens (rows of x) x 64 features (columns of x); the
+// token block varies fastest along the logical block index.
 // Thread (q = tid/8, c8 = tid%8) loads tokens 4q..4q+3, features 8c8..8c8+7,
 // so for each feature it holds four consecutive tokens: one code word.  The
 // per-feature max-abs runs over the 32 threads sharing c8; codes go through
@@ -284,9 +297,10 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
   const int wave = tid >> 6;
   const int c8 = tid & 7;
   const int q = tid >> 3;  // 0..31
-  const int tb = blockIdx.x;
+  const int logical = xcd_block(blockIdx.x, gridDim.x);
+  const int tb = logical % ntb;
   const int t0 = tb * 128;
-  const int f0 = blockIdx.y * 64;
+  const int f0 = (logical / ntb) * 64;
   const bool full = vec && (t0 + 128 <= rows) && (f0 + 64 <= cols);
 
   uint4 v[4];
@@ -454,7 +468,7 @@ hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, b
 hipError_t launch_quant_token_t(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
                                 uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
   const int ntb = (rows + 127) / 128;
-  const dim3 grid(ntb, (cols + 63) / 64), block(256);
+  const dim3 grid(ntb * ((cols + 63) / 64)), block(256);
   const bool vec = ldx % 8 == 0 && ldc % 16 == 0;  // 16-byte loads and stores
   if (pow2) {
     hipLaunchKernelGGL(quant_token_t_kernel<true>, grid, block, 0, stream, x, rows, cols, ldx, codes, ldc, scales, ntb, vec);

@@ -202,10 +202,15 @@ void quantizers() {
   CHECK(last_is("quant_token_t", {300, 72, 80, 0, 304}, {x, codes, scales}));
   EXPECT(fp8q_quantize_act(x, 300, 72, 80, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 299, scales, stream_tag()),
          FP8Q_ERR_SHAPE, false);
-  // features past 65535 grid rows of 64
-  EXPECT(fp8q_quantize_act(x, 128, 65536 * 64 + 1, 65536 * 64 + 1, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 128,
+  // 2^31 tiles or more
+  EXPECT(fp8q_quantize_act(x, 1 << 16, 1 << 24, 1 << 24, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 1 << 16,
                            scales, stream_tag()),
          FP8Q_ERR_SHAPE, false);
+  // 4M features (65536 groups of 64) over 128 token blocks: 2^29 tiles
+  EXPECT(fp8q_quantize_act(x, 1 << 14, 1 << 22, 1 << 22, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 1 << 14,
+                           scales, stream_tag()),
+         FP8Q_OK, true);
+  CHECK(last_is("quant_token_t", {1 << 14, 1 << 22, 1 << 22, 0, 1 << 14}, {x, codes, scales}));
   EXPECT(fp8q_quantize_act(x, int64_t(1) << 31, 8, 8, FP8Q_TILE_ROW, FP8Q_SCALE_FREE, codes, 8, scales, stream_tag()),
          FP8Q_ERR_INVALID_ARG, false);
   EXPECT(fp8q_quantize_act(odd<void>(1), 4, 8, 8, FP8Q_TILE_ROW, FP8Q_SCALE_FREE, codes, 8, scales, stream_tag()),
