@@ -60,7 +60,10 @@ def test_ragged_rows(rows, cols, mode):
     _check_rows(_rand_bits(rng, (rows, cols)), mode, f"ragged {rows}x{cols}")
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (128, 64), (300, 70), (129, 200), (512, 128), (256, 1000)])
+# (700, 900) and (1500, 130): 6 x 15 and 12 x 3 workgroups, counts that the
+# eight XCDs do not divide, so the block order's uneven ranges are covered
+@pytest.mark.parametrize("rows,cols", [(1, 1), (128, 64), (300, 70), (129, 200), (512, 128), (256, 1000),
+                                       (700, 900), (1500, 130)])
 @pytest.mark.parametrize("mode", ["free", "pow2"])
 def test_ragged_token_axis(rows, cols, mode):
     rng = np.random.default_rng(rows * 7 + cols)
