@@ -11,6 +11,10 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxGroups = int64_t(1) << 24;  // 256-thread workgroups per launch
+// 128x128 weight blocks per launch (one workgroup each; with the activation
+// part of fp8q_quantize_linear, at most 2^20 more, still below kMaxGroups)
+constexpr int64_t kMaxWeightBlocks = int64_t(1) << 23;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dim_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
@@ -63,7 +67,10 @@ fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, in
   const int64_t code_row = tile_axis == FP8Q_TILE_ROW ? cols : rows;
   if (ld_codes < code_row) return FP8Q_ERR_SHAPE;
   const int64_t tiles = tile_axis == FP8Q_TILE_ROW ? rows * ((cols + 127) / 128) : cols * ((rows + 127) / 128);
-  if (tiles > kMaxDim) return FP8Q_ERR_SHAPE;  // also bounds the token-axis grid (tiles / 64 + blocks)
+  if (tiles > kMaxDim) return FP8Q_ERR_SHAPE;
+  // a launch's work items (256 per workgroup) must fit in 32 bits
+  if (tile_axis == FP8Q_TILE_TOKEN_T && ((rows + 127) / 128) * ((cols + 63) / 64) >= kMaxGroups)
+    return FP8Q_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
   const bool pow2 = scale_mode == FP8Q_SCALE_POW2;
@@ -80,7 +87,7 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64
   if (N == 0 || K == 0) return FP8Q_OK;
   if (!w_bf16 || !codes || !scales) return FP8Q_ERR_INVALID_ARG;
   if (ld_w < K || ld_codes < K) return FP8Q_ERR_SHAPE;
-  if (((N + 127) / 128) * ((K + 127) / 128) > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (((N + 127) / 128) * ((K + 127) / 128) >= kMaxWeightBlocks) return FP8Q_ERR_SHAPE;
   if (!aligned16(w_bf16) || !aligned16(codes) || !aligned16(scales)) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_quant_blocks(static_cast<const uint16_t*>(w_bf16), (int)N, (int)K, ld_w,
@@ -100,8 +107,7 @@ fp8q_status fp8q_quantize_linear(const void* x_bf16, int64_t M, int64_t K, int64
   if (N > 0 && (!w_bf16 || !w_codes || !w_scales)) return FP8Q_ERR_INVALID_ARG;
   if ((M > 0 && (ld_x < K || ld_a < K)) || (N > 0 && (ld_w < K || ld_wc < K))) return FP8Q_ERR_SHAPE;
   const int64_t nb = (K + 127) / 128;
-  if (M * nb > kMaxDim || ((N + 127) / 128) * nb > kMaxDim || (M * nb + 63) / 64 + ((N + 127) / 128) * nb > kMaxDim)
-    return FP8Q_ERR_SHAPE;
+  if (M * nb > kMaxDim || ((N + 127) / 128) * nb >= kMaxWeightBlocks) return FP8Q_ERR_SHAPE;
   if (M > 0 && (!aligned16(x_bf16) || !aligned16(a_codes) || !aligned16(a_scales))) return FP8Q_ERR_ALIGN;
   if (N > 0 && (!aligned16(w_bf16) || !aligned16(w_codes) || !aligned16(w_scales))) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
@@ -120,7 +126,7 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
   if (N == 0 || K == 0) return FP8Q_OK;
   if (!w_bf16 || !codes_t || !scales_t || (codes && !scales)) return FP8Q_ERR_INVALID_ARG;
   if (ld_w < K || ld_codes_t < N || (codes && ld_codes < K)) return FP8Q_ERR_SHAPE;
-  if (((N + 127) / 128) * ((K + 127) / 128) > kMaxDim) return FP8Q_ERR_SHAPE;
+  if (((N + 127) / 128) * ((K + 127) / 128) >= kMaxWeightBlocks) return FP8Q_ERR_SHAPE;
   if (!aligned16(w_bf16) || !aligned16(codes_t) || !aligned16(scales_t)) return FP8Q_ERR_ALIGN;
   if (codes && (!aligned16(codes) || !aligned16(scales))) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;
@@ -237,6 +243,7 @@ fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, i
   if (rows > 0 && (!codes || !scales)) return FP8Q_ERR_INVALID_ARG;
   if (ld_codes < cols || ld_out < cols) return FP8Q_ERR_SHAPE;
   if (rows * ld_codes >= kMaxOperandBytes || n_out * ld_out >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
+  if ((n_out + 3) / 4 >= kMaxGroups) return FP8Q_ERR_SHAPE;  // one wave per output row
   if (!aligned16(index) || !aligned16(out_codes) || !aligned16(out_scales)) return FP8Q_ERR_ALIGN;
   if (rows > 0 && (!aligned16(codes) || !aligned16(scales))) return FP8Q_ERR_ALIGN;
   if (fp8q_status st = check_device()) return st;

@@ -110,7 +110,9 @@ enum {
  * tile of a row may be ragged) or FP8Q_TILE_TOKEN_T (128x1 along rows; the
  * output is feature-major so a token-axis GEMM reads it K-contiguous).
  * scale_mode: FP8Q_SCALE_FREE or FP8Q_SCALE_POW2.  Codes outside the valid
- * region of each output row are not written. */
+ * region of each output row are not written.  Token tiles: fewer than 2^24
+ * workgroups of 128 tokens x 64 features, else FP8Q_ERR_SHAPE (no input
+ * that fits in device memory reaches it). */
 fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld_x,
                               int tile_axis, int scale_mode,
                               uint8_t* codes, int64_t ld_codes, float* scales,
@@ -119,7 +121,9 @@ fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t rows, int64_t cols, in
 /* Quantize a BF16 weight w[N, K] (row stride ld_w elements) per 128x128
  * block (jp-study.kr doc 258368 ¶1).  codes [N, ld_codes];
  * scales [ceil(N/128), ceil(K/128)] row-major.  Edge blocks may be ragged in
- * both directions. */
+ * both directions.  Fewer than 2^23 blocks (one workgroup each), else
+ * FP8Q_ERR_SHAPE; the same bound holds for fp8q_quantize_linear and
+ * fp8q_quantize_weight_t. */
 fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ld_w,
                                  int scale_mode,
                                  uint8_t* codes, int64_t ld_codes, float* scales,
@@ -226,7 +230,8 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
  * one device; a token may appear several times).  An index outside
  * [0, rows) is not checked on the host (that would need a synchronization):
  * its output row is written as zero codes and a zero scale.  out_codes
- * [n_out, ld_out >= cols], out_scales [n_out, nb]. */
+ * [n_out, ld_out >= cols], out_scales [n_out, nb].  n_out < 2^26 (one wave
+ * per output row), else FP8Q_ERR_SHAPE. */
 fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld_codes,
                              const float* scales, const int32_t* index, int64_t n_out,
                              uint8_t* out_codes, int64_t ld_out, float* out_scales,

@@ -206,6 +206,10 @@ void quantizers() {
   EXPECT(fp8q_quantize_act(x, 1 << 16, 1 << 24, 1 << 24, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 1 << 16,
                            scales, stream_tag()),
          FP8Q_ERR_SHAPE, false);
+  // 2^24 workgroups (128 token blocks x 2^17 feature groups): one too many
+  EXPECT(fp8q_quantize_act(x, 1 << 14, 1 << 23, 1 << 23, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 1 << 14,
+                           scales, stream_tag()),
+         FP8Q_ERR_SHAPE, false);
   // 4M features (65536 groups of 64) over 128 token blocks: 2^29 tiles
   EXPECT(fp8q_quantize_act(x, 1 << 14, 1 << 22, 1 << 22, FP8Q_TILE_TOKEN_T, FP8Q_SCALE_FREE, codes, 1 << 14,
                            scales, stream_tag()),
@@ -223,6 +227,10 @@ void quantizers() {
   CHECK(last_is("quant_blocks", {4096, 7168, 7168, 0, 7168}, {x, codes, scales}));
   EXPECT(fp8q_quantize_weight(x, 4096, 7168, 7168, 2, codes, 7168, scales, stream_tag()), FP8Q_ERR_INVALID_ARG,
          false);
+  // 2^23 blocks of 128 x 128 (2^12 x 2^11 blocks): one workgroup each, too many
+  EXPECT(fp8q_quantize_weight(x, int64_t(1) << 19, int64_t(1) << 18, int64_t(1) << 18, FP8Q_SCALE_FREE, codes,
+                              int64_t(1) << 18, scales, stream_tag()),
+         FP8Q_ERR_SHAPE, false);
 
   const void* w = addr<void>(4);
   auto* wc = addr<uint8_t>(5);
@@ -307,6 +315,11 @@ void moe_glue() {
   CHECK(last_is("gather_rows", {8192, 7168, 7168, 3773, 7168}, {codes, scales, index, out, out_s}));
   EXPECT(fp8q_gather_rows(codes, 8192, 7168, 7168, scales, nullptr, 3773, out, 7168, out_s, stream_tag()),
          FP8Q_ERR_INVALID_ARG, false);
+  // one wave per output row: 2^26 rows (of 16 codes) are too many for one launch
+  EXPECT(fp8q_gather_rows(codes, 8192, 16, 16, scales, index, int64_t(1) << 26, out, 16, out_s, stream_tag()),
+         FP8Q_ERR_SHAPE, false);
+  EXPECT(fp8q_gather_rows(codes, 8192, 16, 16, scales, index, (int64_t(1) << 26) - 4, out, 16, out_s, stream_tag()),
+         FP8Q_OK, true);
 
   const void* x = addr<void>(6);
   auto* ccodes = addr<uint8_t>(7);
