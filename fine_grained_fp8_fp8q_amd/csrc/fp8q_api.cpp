@@ -142,6 +142,9 @@ bool acc_ok(int acc) {
 }
 
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
+// 512-thread GEMM workgroups per launch (work items must fit in 32 bits)
+constexpr int64_t kMaxGemmTiles = int64_t(1) << 23;
+int64_t tiles256(int64_t rows, int64_t cols, int64_t width) { return ((rows + 255) / 256) * ((cols + width - 1) / width); }
 
 fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t ld_c, int64_t N) {
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
@@ -161,7 +164,8 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
-  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
+  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || tiles256(M, N, 256) >= kMaxGemmTiles)
+    return FP8Q_ERR_SHAPE;
   if (K > 0) {
     if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
     if (!aligned16(a) || !aligned16(w) || !aligned16(a_scales) || !aligned16(w_scales)) return FP8Q_ERR_ALIGN;
@@ -181,7 +185,8 @@ fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales, const u
   if (!c_codes || !c_scales) return FP8Q_ERR_INVALID_ARG;
   if (K % 128) return FP8Q_ERR_SHAPE;
   if (ld_c < N) return FP8Q_ERR_SHAPE;
-  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || M * ((N + 127) / 128) > kMaxDim)
+  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || M * ((N + 127) / 128) > kMaxDim ||
+      tiles256(M, N, 256) >= kMaxGemmTiles)
     return FP8Q_ERR_SHAPE;
   if (!aligned16(c_codes) || !aligned16(c_scales)) return FP8Q_ERR_ALIGN;
   if (K > 0) {
@@ -203,7 +208,7 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int
   if (!offsets) return FP8Q_ERR_INVALID_ARG;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
   const int64_t tiles = ((rows_cap + 255) / 256 + G) * ((N + 255) / 256);
-  if (tiles > kMaxDim || rows_cap * K >= kMaxOperandBytes || int64_t(G) * N * K >= kMaxOperandBytes)
+  if (tiles >= kMaxGemmTiles || rows_cap * K >= kMaxOperandBytes || int64_t(G) * N * K >= kMaxOperandBytes)
     return FP8Q_ERR_SHAPE;
   if (K > 0) {
     if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;
@@ -223,7 +228,9 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (Nout == 0 || Kin == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(T, FP8Q_OUT_F32, dw, ld_dw, Kin)) return st;
-  if (Nout * T >= kMaxOperandBytes || Kin * T >= kMaxOperandBytes) return FP8Q_ERR_SHAPE;
+  // tiles of 224 or 256 columns: bound the count with the narrower width
+  if (Nout * T >= kMaxOperandBytes || Kin * T >= kMaxOperandBytes || tiles256(Nout, Kin, 224) >= kMaxGemmTiles)
+    return FP8Q_ERR_SHAPE;
   if (T > 0) {
     if (!dy_t || !dy_scales || !x_t || !x_scales) return FP8Q_ERR_INVALID_ARG;
     if (!aligned16(dy_t) || !aligned16(x_t) || !aligned16(dy_scales) || !aligned16(x_scales)) return FP8Q_ERR_ALIGN;

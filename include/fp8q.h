@@ -166,7 +166,10 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
  * contiguous; w_scales [ceil(N/128), K/128].  K must be a multiple of 128
  * (K = 0 writes zeros).  out_dtype FP8Q_OUT_F32 (c is float*) or
  * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); acc one
- * of the FP8Q_ACC_* forms; row stride ld_c elements.  C is overwritten. */
+ * of the FP8Q_ACC_* forms; row stride ld_c elements.  C is overwritten.
+ * Each code operand is below 2 GiB, and fewer than 2^23 output tiles of
+ * 256 x 256 (one workgroup each; for the grouped and weight-gradient forms
+ * the tile counts they launch), else FP8Q_ERR_SHAPE. */
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       const uint8_t* w, const float* w_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype, int acc,

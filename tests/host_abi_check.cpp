@@ -270,6 +270,10 @@ void gemms() {
   // an operand of 2 GiB or more (32-bit byte offsets in the kernels)
   EXPECT(fp8q_gemm(a, sa, w, sw, 1 << 24, 4, 128, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()), FP8Q_ERR_SHAPE,
          false);
+  // 2^23 tiles of 256 x 256 (2^12 x 2^11): too many workgroups for one launch
+  EXPECT(fp8q_gemm(a, sa, w, sw, int64_t(1) << 20, int64_t(1) << 19, 0, FP8Q_OUT_F32, FP8Q_ACC_FP32, c,
+                   int64_t(1) << 19, stream_tag()),
+         FP8Q_ERR_SHAPE, false);
   // K = 0: C = 0 is written by the kernel, operand pointers may be null
   EXPECT(fp8q_gemm(nullptr, nullptr, nullptr, nullptr, 4, 4, 0, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()),
          FP8Q_OK, true);
