@@ -253,13 +253,13 @@ def moe_rates(torch, fp8q, lib, stream, reps):
 
     def ffn(i):
         st = fg(i)
-        st = st or lib.fp8q_grouped_gemm(a_up.data_ptr(), s_up.data_ptr(), off.data_ptr(), G, rows,
+        st = st or lib.fp8q_grouped_gemm_ex(a_up.data_ptr(), s_up.data_ptr(), off.data_ptr(), G, rows,
                                          wq_u.data_ptr(), ws_u.data_ptr(), n_u, k_u, fp8q.OUT_BF16,
                                          fp8q.ACC_FP32, up_out.data_ptr(), n_u, stream.cuda_stream)
         st = st or lib.fp8q_swiglu_quantize(up_out.data_ptr(), rows, inter, n_u, fp8q.SCALE_FREE,
                                             sq.data_ptr(), inter, ss.data_ptr(), fp8q.SCALE_POW2, None, 0,
                                             None, stream.cuda_stream)
-        st = st or lib.fp8q_grouped_gemm(sq.data_ptr(), ss.data_ptr(), off.data_ptr(), G, rows,
+        st = st or lib.fp8q_grouped_gemm_ex(sq.data_ptr(), ss.data_ptr(), off.data_ptr(), G, rows,
                                          wq_d.data_ptr(), ws_d.data_ptr(), n_d, k_d, fp8q.OUT_BF16,
                                          fp8q.ACC_FP32, y.data_ptr(), n_d, stream.cuda_stream)
         return st
@@ -274,7 +274,7 @@ def _grouped_rate(torch, lib, stream, reps, counts, in_a, in_s, off, G, rows, wq
     """Grouped GEMM time for one accumulation mode, with the whole-kernel and
     the per-expert roofline."""
     def fn(i):
-        return lib.fp8q_grouped_gemm(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
+        return lib.fp8q_grouped_gemm_ex(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
                                      wq.data_ptr(), ws.data_ptr(), n, k, fp8q.OUT_BF16, acc, c.data_ptr(),
                                      n, stream.cuda_stream)
     us = _event_us(torch, stream, fn, reps)
@@ -325,7 +325,7 @@ def wgrad_rates(torch, fp8q, lib, stream, reps):
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
     for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
         def fg(i, acc=acc):
-            return lib.fp8q_wgrad(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
+            return lib.fp8q_wgrad_ex(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
                                   acc, dw.data_ptr(), kin, stream.cuda_stream)
         us = _event_us(torch, stream, fg, reps)
         out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = _roofline(flop, nbytes, us)
@@ -364,7 +364,7 @@ def dgrad_rates(torch, fp8q, lib, stream, reps, w):
     nbytes = m * n + n * k + m * (n // 128) * 4 + (k // 128) * (n // 128) * 4 + m * k * 2
     for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
         def fg(i, acc=acc):
-            return lib.fp8q_gemm(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k,
+            return lib.fp8q_gemm_ex(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k,
                                  n, fp8q.OUT_BF16, acc, dx.data_ptr(), k, stream.cuda_stream)
         out[f"dgrad_{m}x{k}x{n}{acc_name}"] = _roofline(flop, nbytes, _event_us(torch, stream, fg, reps))
     return out
@@ -466,7 +466,7 @@ def main():
     sp = stream.cuda_stream
 
     def gemm():
-        return lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
+        return lib.fp8q_gemm_ex(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
                              M, N, K, fp8q.OUT_BF16, fp8q.ACC_FP32, c.data_ptr(), N, sp)
 
     def q_both():
@@ -538,14 +538,14 @@ def main():
                                         N, K, fp8q.SCALE_FREE, wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
     ql_us = kernel_us(q_lin_i)
     gemm_us = kernel_us(lambda i: gemm())
-    gemm_f8_us = kernel_us(lambda i: lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
+    gemm_f8_us = kernel_us(lambda i: lib.fp8q_gemm_ex(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
                                                    w_scales.data_ptr(), M, N, K, fp8q.OUT_BF16,
                                                    fp8q.ACC_FP8_MFMA, c.data_ptr(), N, sp))
     # the hardware-scaled form needs power-of-two scales: the same inputs
     # quantized in that mode
     ap_codes, ap_scales = fp8q.quantize_act(a, scale_mode="pow2")
     wp_codes, wp_scales = fp8q.quantize_weight(w, scale_mode="pow2")
-    gemm_f8s_us = kernel_us(lambda i: lib.fp8q_gemm(ap_codes.data_ptr(), ap_scales.data_ptr(),
+    gemm_f8s_us = kernel_us(lambda i: lib.fp8q_gemm_ex(ap_codes.data_ptr(), ap_scales.data_ptr(),
                                                     wp_codes.data_ptr(), wp_scales.data_ptr(), M, N, K,
                                                     fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA_SCALED, c.data_ptr(), N, sp))
     del ap_codes, ap_scales, wp_codes, wp_scales

@@ -18,6 +18,10 @@ Functions (names follow the C ABI without the ``fp8q_`` prefix):
 * ``gemm(a, a_scales, w, w_scales, out_dtype=torch.bfloat16|torch.float32)``
 * ``grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=...)``
 * ``wgrad(dy_t, dy_scales, x_t, x_scales)``
+
+  The three GEMMs call ``fp8q_gemm`` / ``fp8q_grouped_gemm`` / ``fp8q_wgrad``
+  (partials at float32 grade); ``acc="fp8_mfma"`` or ``"fp8_mfma_scaled"``
+  calls the ``_ex`` entry point with that accumulation form.
 * ``gemm_quantized(a, a_scales, w, w_scales, scale_mode=...)`` -> (codes, scales)
   of C rounded to BF16 and quantized per 1x128 tile along N
 * ``gather_rows(codes, scales, index)`` -> (codes, scales) of rows ``index``
@@ -38,8 +42,8 @@ ACC_FP32, ACC_FP8_MFMA, ACC_FP8_MFMA_SCALED = 0, 1, 2
 TILE_ROW, TILE_TOKEN_T = 0, 1
 
 SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_linear", "fp8q_quantize_weight_t", "fp8q_gemm",
-           "fp8q_gemm_quantized", "fp8q_grouped_gemm", "fp8q_wgrad", "fp8q_gather_rows",
-           "fp8q_swiglu_quantize",
+           "fp8q_gemm_ex", "fp8q_gemm_quantized", "fp8q_grouped_gemm", "fp8q_grouped_gemm_ex", "fp8q_wgrad",
+           "fp8q_wgrad_ex", "fp8q_gather_rows", "fp8q_swiglu_quantize",
            "fp8q_status_string")
 
 _lib = None
@@ -65,10 +69,13 @@ def load_library(path=None):
     lib.fp8q_quantize_weight.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_linear.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, i64, ip, vp, i64, vp, vp]
     lib.fp8q_quantize_weight_t.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, vp, i64, vp, vp]
-    lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
+    lib.fp8q_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_gemm_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp]
     lib.fp8q_gemm_quantized.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, ip, vp, i64, vp, vp]
-    lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, ip, vp, i64, vp]
-    lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_grouped_gemm.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, vp, i64, vp]
+    lib.fp8q_grouped_gemm_ex.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, ip, ip, vp, i64, vp]
+    lib.fp8q_wgrad.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.fp8q_wgrad_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
     lib.fp8q_gather_rows.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp]
     lib.fp8q_swiglu_quantize.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, ip, vp, i64, vp, vp]
     for name in SYMBOLS[:-1]:
@@ -278,8 +285,13 @@ def gemm(a, a_scales, w, w_scales, out_dtype=None, out=None, acc="fp32"):
     if w.shape[1] != k or a_scales.shape != (m, k // 128) or w_scales.shape != ((n + 127) // 128, k // 128):
         raise ValueError("operand shapes do not match")
     c = out if out is not None else torch.empty((m, n), dtype=out_dtype, device=a.device)
-    st = load_library().fp8q_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), m, n, k,
-                                  _out_code(c.dtype), _acc_code(acc), _ptr(c), c.stride(0), _stream(a))
+    lib, code = load_library(), _acc_code(acc)
+    if code == ACC_FP32:
+        st = lib.fp8q_gemm(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), m, n, k, _out_code(c.dtype), _ptr(c),
+                           c.stride(0), _stream(a))
+    else:
+        st = lib.fp8q_gemm_ex(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), m, n, k, _out_code(c.dtype), code,
+                              _ptr(c), c.stride(0), _stream(a))
     _check(st, "fp8q_gemm")
     return c
 
@@ -332,9 +344,14 @@ def grouped_gemm(a, a_scales, offsets, w, w_scales, out_dtype=None, out=None, ac
     if kw != k or offsets.numel() != g + 1:
         raise ValueError("operand shapes do not match")
     c = out if out is not None else torch.empty((rows_cap, n), dtype=out_dtype, device=a.device)
-    st = load_library().fp8q_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(offsets), g, rows_cap, _ptr(w),
-                                          _ptr(w_scales), n, k, _out_code(c.dtype), _acc_code(acc), _ptr(c),
-                                          c.stride(0), _stream(a))
+    lib, code = load_library(), _acc_code(acc)
+    if code == ACC_FP32:
+        st = lib.fp8q_grouped_gemm(_ptr(a), _ptr(a_scales), _ptr(offsets), g, rows_cap, _ptr(w), _ptr(w_scales), n,
+                                   k, _out_code(c.dtype), _ptr(c), c.stride(0), _stream(a))
+    else:
+        st = lib.fp8q_grouped_gemm_ex(_ptr(a), _ptr(a_scales), _ptr(offsets), g, rows_cap, _ptr(w),
+                                      _ptr(w_scales), n, k, _out_code(c.dtype), code, _ptr(c), c.stride(0),
+                                      _stream(a))
     _check(st, "fp8q_grouped_gemm")
     return c
 
@@ -351,8 +368,13 @@ def wgrad(dy_t, dy_scales, x_t, x_scales, out=None, acc="fp32"):
     if x_t.shape[1] != t:
         raise ValueError("operand shapes do not match")
     dw = out if out is not None else torch.empty((nout, kin), dtype=torch.float32, device=dy_t.device)
-    st = load_library().fp8q_wgrad(_ptr(dy_t), _ptr(dy_scales), _ptr(x_t), _ptr(x_scales), nout, kin, t,
-                                   _acc_code(acc), _ptr(dw), dw.stride(0), _stream(dy_t))
+    lib, code = load_library(), _acc_code(acc)
+    if code == ACC_FP32:
+        st = lib.fp8q_wgrad(_ptr(dy_t), _ptr(dy_scales), _ptr(x_t), _ptr(x_scales), nout, kin, t, _ptr(dw),
+                            dw.stride(0), _stream(dy_t))
+    else:
+        st = lib.fp8q_wgrad_ex(_ptr(dy_t), _ptr(dy_scales), _ptr(x_t), _ptr(x_scales), nout, kin, t, code,
+                               _ptr(dw), dw.stride(0), _stream(dy_t))
     _check(st, "fp8q_wgrad")
     return dw
 

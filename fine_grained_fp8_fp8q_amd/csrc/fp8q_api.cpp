@@ -156,9 +156,9 @@ fp8q_status check_gemm_common(int64_t K, int out_dtype, const void* c, int64_t l
 }
 }  // namespace
 
-fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
-                      int64_t M, int64_t N, int64_t K, int out_dtype, int acc, void* c, int64_t ld_c,
-                      hipStream_t stream) {
+fp8q_status fp8q_gemm_ex(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
+                         int64_t M, int64_t N, int64_t K, int out_dtype, int acc, void* c, int64_t ld_c,
+                         hipStream_t stream) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
@@ -173,6 +173,11 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_gemm(a, a_scales, w, w_scales, (int)M, (int)N, (int)K,
                                     out_dtype == FP8Q_OUT_BF16, acc, c, ld_c, stream));
+}
+
+fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
+                      int64_t M, int64_t N, int64_t K, int out_dtype, void* c, int64_t ld_c, hipStream_t stream) {
+  return fp8q_gemm_ex(a, a_scales, w, w_scales, M, N, K, out_dtype, FP8Q_ACC_FP32, c, ld_c, stream);
 }
 
 fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
@@ -198,9 +203,9 @@ fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales, const u
                                               scale_mode == FP8Q_SCALE_POW2, c_codes, ld_c, c_scales, stream));
 }
 
-fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
-                              int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N,
-                              int64_t K, int out_dtype, int acc, void* c, int64_t ld_c, hipStream_t stream) {
+fp8q_status fp8q_grouped_gemm_ex(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
+                                 int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N,
+                                 int64_t K, int out_dtype, int acc, void* c, int64_t ld_c, hipStream_t stream) {
   if (G < 0 || !dim_ok(rows_cap) || !dim_ok(N) || !dim_ok(K) || !dim_ok(ld_c)) return FP8Q_ERR_INVALID_ARG;
   if (out_dtype != FP8Q_OUT_F32 && out_dtype != FP8Q_OUT_BF16) return FP8Q_ERR_INVALID_ARG;
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
@@ -221,9 +226,16 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int
                                             ld_c, stream));
 }
 
-fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t, const float* x_scales,
-                       int64_t Nout, int64_t Kin, int64_t T, int acc, float* dw, int64_t ld_dw,
-                       hipStream_t stream) {
+fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales, const int32_t* offsets, int32_t G,
+                              int64_t rows_cap, const uint8_t* w, const float* w_scales, int64_t N, int64_t K,
+                              int out_dtype, void* c, int64_t ld_c, hipStream_t stream) {
+  return fp8q_grouped_gemm_ex(a, a_scales, offsets, G, rows_cap, w, w_scales, N, K, out_dtype, FP8Q_ACC_FP32, c,
+                              ld_c, stream);
+}
+
+fp8q_status fp8q_wgrad_ex(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t, const float* x_scales,
+                          int64_t Nout, int64_t Kin, int64_t T, int acc, float* dw, int64_t ld_dw,
+                          hipStream_t stream) {
   if (!dim_ok(Nout) || !dim_ok(Kin) || !dim_ok(T) || !dim_ok(ld_dw)) return FP8Q_ERR_INVALID_ARG;
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (Nout == 0 || Kin == 0) return FP8Q_OK;
@@ -238,6 +250,11 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_
   if (fp8q_status st = check_device()) return st;
   return launched(fp8q::launch_wgrad(dy_t, dy_scales, x_t, x_scales, (int)Nout, (int)Kin, (int)T,
                                      acc, dw, ld_dw, stream));
+}
+
+fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8_t* x_t, const float* x_scales,
+                       int64_t Nout, int64_t Kin, int64_t T, float* dw, int64_t ld_dw, hipStream_t stream) {
+  return fp8q_wgrad_ex(dy_t, dy_scales, x_t, x_scales, Nout, Kin, T, FP8Q_ACC_FP32, dw, ld_dw, stream);
 }
 
 fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld_codes,

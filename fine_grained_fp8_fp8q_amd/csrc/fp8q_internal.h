@@ -7,6 +7,23 @@
 
 namespace fp8q {
 
+// Grid sizes of the streaming kernels (host code; 64-bit arithmetic, so a
+// tile count up to 2^31 - 1 cannot overflow here).
+//  rows_grid: the 1x128 row quantizer, one pass per wave (64 tiles per
+//    256-thread workgroup) up to kMaxRowsGrid workgroups, then a grid-stride
+//    loop whose stride is 64 * kMaxRowsGrid tiles.
+//  stream_grid: four waves per workgroup, up to kMaxStreamGrid workgroups.
+constexpr int kMaxRowsGrid = 1 << 20;
+constexpr int kMaxStreamGrid = 2048;
+inline int rows_grid(int64_t ntiles) {
+  const int64_t want = (ntiles + 63) / 64;
+  return (int)(want < kMaxRowsGrid ? want : kMaxRowsGrid);
+}
+inline int stream_grid(int64_t waves_needed) {
+  const int64_t wg = (waves_needed + 3) / 4;
+  return (int)(wg < kMaxStreamGrid ? (wg > 0 ? wg : 1) : kMaxStreamGrid);
+}
+
 // Launchers validate nothing: fp8q_api.cpp has checked shapes, alignment and
 // the device before calling them.  Every size here is > 0 and < 2^31.
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,

@@ -156,8 +156,12 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& g, Tile& t) {
     int mt = bid / g.tiles_n;
     for (int cls = 0; cls < 3; ++cls) {
       for (int gi = 0; gi < g.groups; ++gi) {
-        const int lo = g.offsets[gi], hi = g.offsets[gi + 1];
-        const int rows = hi > lo ? hi - lo : 0;
+        // a routing table that breaks its precondition (offsets outside
+        // [0, rows_cap] or decreasing) is clamped: every tile stays inside
+        // the rows of a and c
+        const int lo = min(max(g.offsets[gi], 0), g.rows);
+        const int hi = min(max(g.offsets[gi + 1], lo), g.rows);
+        const int rows = hi - lo;
         const int full = rows / BM, rem = rows % BM;
         const int cnt = cls == 0 ? full + (rem > 128 ? 1 : 0)
                       : cls == 1 ? (rem > 64 && rem <= 128 ? 1 : 0)

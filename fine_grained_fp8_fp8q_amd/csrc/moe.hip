@@ -128,19 +128,21 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int sub = lane & 15;
-  const int wave = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
-  const int nwaves = (int)(gridDim.x * 4u);
+  // 32-bit unsigned tile indices: ntiles < 2^31 and the stride is at most
+  // 4 * kSwU * 4 * kMaxStreamGrid, so base + stride never wraps.
+  const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
+  const uint32_t step = gridDim.x * 16u * kSwU;
 
-  for (int base = wave * 4 * kSwU; base < ntiles; base += nwaves * 4 * kSwU) {
+  for (uint32_t base = wave * 4u * kSwU; base < (uint32_t)ntiles; base += step) {
     uint4 gv[kSwU], uv[kSwU];
     int row[kSwU], col[kSwU], nvalid[kSwU];
     bool valid[kSwU], full[kSwU];
 #pragma unroll
     for (int u = 0; u < kSwU; ++u) {
-      const int t = base + u * 4 + grp;
-      valid[u] = t < ntiles;
-      row[u] = valid[u] ? t / nb : 0;
-      const int cb = valid[u] ? t - row[u] * nb : 0;
+      const uint32_t t = base + (uint32_t)(u * 4 + grp);
+      valid[u] = t < (uint32_t)ntiles;
+      row[u] = valid[u] ? (int)(t / (uint32_t)nb) : 0;
+      const int cb = valid[u] ? (int)(t - (uint32_t)row[u] * (uint32_t)nb) : 0;
       col[u] = cb * 128 + sub * 8;
       nvalid[u] = valid[u] ? inter - col[u] : 0;
       full[u] = vec && valid[u] && (cb * 128 + 128 <= inter);
@@ -173,20 +175,15 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
 
 namespace {
 
-int stream_grid(int64_t waves_needed) {
-  // four waves per workgroup; at most 8 workgroups per CU in flight
-  const int64_t wg = (waves_needed + 3) / 4;
-  return (int)(wg < 2048 ? (wg > 0 ? wg : 1) : 2048);
-}
-
 template <bool POW2, bool CACHE, bool CPOW2>
 hipError_t launch_swiglu(const uint16_t* x, int rows, int inter, int64_t ldx, uint8_t* codes, int64_t ldc,
                          float* scales, uint8_t* ccodes, int64_t ldcc, float* cscales, hipStream_t stream) {
   const int nb = (inter + 127) / 128;
-  const int ntiles = rows * nb;
+  const int ntiles = rows * nb;  // < 2^31 (checked by the entry point)
   const bool vec = (ldx % 8 == 0) && (inter % 8 == 0) && (ldc % 8 == 0) && (!CACHE || ldcc % 8 == 0);
-  hipLaunchKernelGGL((swiglu_quant_kernel<POW2, CACHE, CPOW2>), dim3(stream_grid((ntiles + 4 * kSwU - 1) / (4 * kSwU))), dim3(256),
-                     0, stream, x, inter, ldx, codes, ldc, scales, ccodes, ldcc, cscales, nb, ntiles, vec);
+  const int64_t waves = ((int64_t)ntiles + 4 * kSwU - 1) / (4 * kSwU);
+  hipLaunchKernelGGL((swiglu_quant_kernel<POW2, CACHE, CPOW2>), dim3(stream_grid(waves)), dim3(256), 0, stream, x,
+                     inter, ldx, codes, ldc, scales, ccodes, ldcc, cscales, nb, ntiles, vec);
   return hipGetLastError();
 }
 

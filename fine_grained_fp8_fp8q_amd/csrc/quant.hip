@@ -23,19 +23,21 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int sub = lane & 15;
-  const int wave = (int)(((unsigned)bid * 256u + threadIdx.x) >> 6);
-  const int nwaves = nblocks * 4;
+  // Tile indices count in 32-bit unsigned: ntiles < 2^31 and the stride is
+  // at most 16 * 4 * kMaxRowsGrid = 2^26, so base + stride never wraps.
+  const uint32_t wave = ((uint32_t)bid * 256u + threadIdx.x) >> 6;
+  const uint32_t step = (uint32_t)nblocks * 64u;
 
-  for (int base = wave * 16; base < ntiles; base += nwaves * 16) {
+  for (uint32_t base = wave * 16u; base < (uint32_t)ntiles; base += step) {
     uint4 v[4];
     int row[4], cb[4];
     bool valid[4], full[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = base + u * 4 + grp;
-      valid[u] = t < ntiles;
-      row[u] = valid[u] ? t / nb : 0;
-      cb[u] = valid[u] ? t - row[u] * nb : 0;
+      const uint32_t t = base + (uint32_t)(u * 4 + grp);
+      valid[u] = t < (uint32_t)ntiles;
+      row[u] = valid[u] ? (int)(t / (uint32_t)nb) : 0;
+      cb[u] = valid[u] ? (int)(t - (uint32_t)row[u] * (uint32_t)nb) : 0;
       full[u] = vec && valid[u] && (cb[u] * 128 + 128 <= cols);
       const uint16_t* src = x + (int64_t)row[u] * ldx + cb[u] * 128 + sub * 8;
       if (full[u]) {
@@ -390,14 +392,10 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------ launchers ---
-// One pass per wave (64 tiles per 256-thread workgroup): a large grid keeps
-// more loads in flight than a grid-stride loop over a capped grid (measured
-// on MI355X: 4.7 TB/s at 2048 workgroups vs 5.8 TB/s with one pass for this
-// 2:1 read:write stream).
-static int rows_grid(int ntiles) {
-  const int want = (ntiles + 63) / 64;
-  return want < (1 << 20) ? want : (1 << 20);
-}
+// rows_grid (fp8q_internal.h): one pass per wave (64 tiles per 256-thread
+// workgroup) up to 2^20 workgroups; a large grid keeps more loads in flight
+// than a grid-stride loop over a capped grid (measured on MI355X: 4.7 TB/s at
+// 2048 workgroups vs 5.8 TB/s with one pass for this 2:1 read:write stream).
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
                              uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {

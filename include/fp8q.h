@@ -165,15 +165,25 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
  * a: codes [M, K] contiguous; a_scales [M, K/128]; w: codes [N, K]
  * contiguous; w_scales [ceil(N/128), K/128].  K must be a multiple of 128
  * (K = 0 writes zeros).  out_dtype FP8Q_OUT_F32 (c is float*) or
- * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); acc one
- * of the FP8Q_ACC_* forms; row stride ld_c elements.  C is overwritten.
+ * FP8Q_OUT_BF16 (c holds BF16 patterns, rounded to nearest even); row
+ * stride ld_c elements.  C is overwritten.  Partials are formed at float32
+ * grade (FP8Q_ACC_FP32): |C - exact| <= 1e-5 * sum|a*b| + 1e-6.
  * Each code operand is below 2 GiB, and fewer than 2^23 output tiles of
  * 256 x 256 (one workgroup each; for the grouped and weight-gradient forms
  * the tile counts they launch), else FP8Q_ERR_SHAPE. */
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       const uint8_t* w, const float* w_scales,
-                      int64_t M, int64_t N, int64_t K, int out_dtype, int acc,
+                      int64_t M, int64_t N, int64_t K, int out_dtype,
                       void* c, int64_t ld_c, hipStream_t stream);
+
+/* fp8q_gemm with the accumulation form chosen by the caller: acc is one of
+ * the FP8Q_ACC_* values above (fp8q_gemm is fp8q_gemm_ex with
+ * FP8Q_ACC_FP32).  Same arguments, layouts and errors otherwise; an unknown
+ * acc gives FP8Q_ERR_INVALID_ARG. */
+fp8q_status fp8q_gemm_ex(const uint8_t* a, const float* a_scales,
+                         const uint8_t* w, const float* w_scales,
+                         int64_t M, int64_t N, int64_t K, int out_dtype, int acc,
+                         void* c, int64_t ld_c, hipStream_t stream);
 
 /* fp8q_gemm with its output quantized in the epilogue, for a consumer that
  * takes FP8 input (tmdrlife.com wr_id=13334 ¶1: the BF16 output of one
@@ -185,7 +195,7 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
  * (FP8Q_TILE_ROW, scale_mode) quantizes it: the result is bit for bit the
  * unfused fp8q_gemm(FP8Q_OUT_BF16) followed by fp8q_quantize_act, without
  * the BF16 round trip through HBM.
- * a, a_scales, w, w_scales, M, N, K, acc as for fp8q_gemm; c_codes
+ * a, a_scales, w, w_scales, M, N, K as for fp8q_gemm, acc as for fp8q_gemm_ex; c_codes
  * [M, ld_c >= N] E4M3; c_scales [M, ceil(N/128)] float32. */
 fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales,
                                 const uint8_t* w, const float* w_scales,
@@ -203,24 +213,43 @@ fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales,
  *   synchronization); empty groups are allowed;
  * w: codes [G, N, K]; w_scales [G, ceil(N/128), K/128];
  * c: [rows_cap, ld_c] in grouped (expert-sorted) row order; rows not
- * covered by any group are not written.  out_dtype and acc as for fp8q_gemm. */
+ * covered by any group are not written.  out_dtype as for fp8q_gemm; the
+ * partials are formed at float32 grade.
+ * The kernel clamps every group's row range to [0, rows_cap] (a routing table
+ * that breaks the precondition gives wrong rows for the groups it breaks,
+ * never an access outside a or c). */
 fp8q_status fp8q_grouped_gemm(const uint8_t* a, const float* a_scales,
                               const int32_t* offsets, int32_t G, int64_t rows_cap,
                               const uint8_t* w, const float* w_scales,
-                              int64_t N, int64_t K, int out_dtype, int acc,
+                              int64_t N, int64_t K, int out_dtype,
                               void* c, int64_t ld_c, hipStream_t stream);
+
+/* fp8q_grouped_gemm with the accumulation form acc (FP8Q_ACC_*), as
+ * fp8q_gemm_ex extends fp8q_gemm. */
+fp8q_status fp8q_grouped_gemm_ex(const uint8_t* a, const float* a_scales,
+                                 const int32_t* offsets, int32_t G, int64_t rows_cap,
+                                 const uint8_t* w, const float* w_scales,
+                                 int64_t N, int64_t K, int out_dtype, int acc,
+                                 void* c, int64_t ld_c, hipStream_t stream);
 
 /* FP8 weight gradient dW[Nout, Kin] = dY^T . X over T tokens
  * (jp-study.kr doc 258368 ¶3):
  *   dW[n,c] = sum_b dy_scales[n,b] * x_scales[c,b] * sum_{t in block b} dY[t,n] * X[t,c]
  * Operands are FP8Q_TILE_TOKEN_T outputs with ld_codes = T: dy_t codes
  * [Nout, T], dy_scales [Nout, T/128], x_t codes [Kin, T], x_scales
- * [Kin, T/128].  T must be a multiple of 128 (T = 0 writes zeros).  acc as
- * for fp8q_gemm.  Output float32, row stride ld_dw elements, overwritten. */
+ * [Kin, T/128].  T must be a multiple of 128 (T = 0 writes zeros).  Partials
+ * at float32 grade.  Output float32, row stride ld_dw elements, overwritten. */
 fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
                        const uint8_t* x_t, const float* x_scales,
-                       int64_t Nout, int64_t Kin, int64_t T, int acc,
+                       int64_t Nout, int64_t Kin, int64_t T,
                        float* dw, int64_t ld_dw, hipStream_t stream);
+
+/* fp8q_wgrad with the accumulation form acc (FP8Q_ACC_*), as fp8q_gemm_ex
+ * extends fp8q_gemm. */
+fp8q_status fp8q_wgrad_ex(const uint8_t* dy_t, const float* dy_scales,
+                          const uint8_t* x_t, const float* x_scales,
+                          int64_t Nout, int64_t Kin, int64_t T, int acc,
+                          float* dw, int64_t ld_dw, hipStream_t stream);
 
 /* FP8 dispatch gather (jp-study.kr doc 258368 ¶1: activations are quantized
  * once, before the MoE dispatch, and the FP8 codes travel instead of BF16).
@@ -233,8 +262,9 @@ fp8q_status fp8q_wgrad(const uint8_t* dy_t, const float* dy_scales,
  * one device; a token may appear several times).  An index outside
  * [0, rows) is not checked on the host (that would need a synchronization):
  * its output row is written as zero codes and a zero scale.  out_codes
- * [n_out, ld_out >= cols], out_scales [n_out, nb].  n_out < 2^26 (one wave
- * per output row), else FP8Q_ERR_SHAPE. */
+ * [n_out, ld_out >= cols], out_scales [n_out, nb].  n_out <= 2^26 - 4 (one
+ * wave per output row, four per workgroup, fewer than 2^24 workgroups), else
+ * FP8Q_ERR_SHAPE. */
 fp8q_status fp8q_gather_rows(const uint8_t* codes, int64_t rows, int64_t cols, int64_t ld_codes,
                              const float* scales, const int32_t* index, int64_t n_out,
                              uint8_t* out_codes, int64_t ld_out, float* out_scales,

@@ -6,6 +6,7 @@
 // the device check and its per-device cache, the hand-over of each argument
 // to its launcher, and the mapping of a failed launch to FP8Q_ERR_LAUNCH.
 // Prints "host ABI checks passed" and returns 0 when every check holds.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -161,7 +162,7 @@ void device_check() {
   const auto* w = addr<uint8_t>(3);
   const auto* sw = addr<float>(4);
   void* c = addr<void>(5);
-  auto gemm = [&] { return fp8q_gemm(a, sa, w, sw, 256, 256, 256, FP8Q_OUT_BF16, FP8Q_ACC_FP32, c, 256, stream_tag()); };
+  auto gemm = [&] { return fp8q_gemm(a, sa, w, sw, 256, 256, 256, FP8Q_OUT_BF16, c, 256, stream_tag()); };
   g_dev = -1;
   EXPECT(gemm(), FP8Q_ERR_DEVICE, false);
   // another architecture: refused, and the answer is cached per device
@@ -262,23 +263,29 @@ void gemms() {
   const auto* w = addr<uint8_t>(3);
   const auto* sw = addr<float>(4);
   void* c = addr<void>(5);
-  EXPECT(fp8q_gemm(a, sa, w, sw, 4096, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP8_MFMA, c, 4104, stream_tag()), FP8Q_OK,
-         true);
+  // the plain entry point runs the float32-grade form
+  EXPECT(fp8q_gemm(a, sa, w, sw, 4096, 4096, 7168, FP8Q_OUT_BF16, c, 4104, stream_tag()), FP8Q_OK, true);
+  CHECK(last_is("gemm", {4096, 4096, 7168, 1, FP8Q_ACC_FP32, 4104}, {a, sa, w, sw, c}));
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4096, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP8_MFMA, c, 4104, stream_tag()),
+         FP8Q_OK, true);
   CHECK(last_is("gemm", {4096, 4096, 7168, 1, FP8Q_ACC_FP8_MFMA, 4104}, {a, sa, w, sw, c}));
-  EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 100, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()), FP8Q_ERR_SHAPE, false);
-  EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 128, FP8Q_OUT_F32, 3, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
-  // an operand of 2 GiB or more (32-bit byte offsets in the kernels)
-  EXPECT(fp8q_gemm(a, sa, w, sw, 1 << 24, 4, 128, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()), FP8Q_ERR_SHAPE,
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 64, 32, 256, FP8Q_OUT_F32, FP8Q_ACC_FP8_MFMA_SCALED, c, 32, stream_tag()), FP8Q_OK,
+         true);
+  CHECK(last_is("gemm", {64, 32, 256, 0, FP8Q_ACC_FP8_MFMA_SCALED, 32}, {a, sa, w, sw, c}));
+  EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 100, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_ERR_SHAPE, false);
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4, 4, 100, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()), FP8Q_ERR_SHAPE,
          false);
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4, 4, 128, FP8Q_OUT_F32, 3, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
+  EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 128, 2, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
+  // an operand of 2 GiB or more (32-bit byte offsets in the kernels)
+  EXPECT(fp8q_gemm(a, sa, w, sw, 1 << 24, 4, 128, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_ERR_SHAPE, false);
   // 2^23 tiles of 256 x 256 (2^12 x 2^11): too many workgroups for one launch
-  EXPECT(fp8q_gemm(a, sa, w, sw, int64_t(1) << 20, int64_t(1) << 19, 0, FP8Q_OUT_F32, FP8Q_ACC_FP32, c,
-                   int64_t(1) << 19, stream_tag()),
+  EXPECT(fp8q_gemm(a, sa, w, sw, int64_t(1) << 20, int64_t(1) << 19, 0, FP8Q_OUT_F32, c, int64_t(1) << 19,
+                   stream_tag()),
          FP8Q_ERR_SHAPE, false);
   // K = 0: C = 0 is written by the kernel, operand pointers may be null
-  EXPECT(fp8q_gemm(nullptr, nullptr, nullptr, nullptr, 4, 4, 0, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()),
-         FP8Q_OK, true);
-  EXPECT(fp8q_gemm(a, sa, w, odd<float>(4), 4, 4, 128, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()),
-         FP8Q_ERR_ALIGN, false);
+  EXPECT(fp8q_gemm(nullptr, nullptr, nullptr, nullptr, 4, 4, 0, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_OK, true);
+  EXPECT(fp8q_gemm(a, sa, w, odd<float>(4), 4, 4, 128, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_ERR_ALIGN, false);
 
   auto* cc = addr<uint8_t>(6);
   auto* cs = addr<float>(7);
@@ -287,25 +294,31 @@ void gemms() {
   CHECK(last_is("gemm_quantized", {100, 384, 256, FP8Q_ACC_FP32, 1, 384}, {a, sa, w, sw, cc, cs}));
 
   const auto* offs = addr<int32_t>(8);
-  EXPECT(fp8q_grouped_gemm(a, sa, offs, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP32, c, 4096,
-                           stream_tag()),
-         FP8Q_OK, true);
+  EXPECT(fp8q_grouped_gemm(a, sa, offs, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, c, 4096, stream_tag()), FP8Q_OK,
+         true);
   CHECK(last_is("grouped_gemm", {16, 8776, 4096, 7168, 1, FP8Q_ACC_FP32, 4096}, {a, sa, offs, w, sw, c}));
-  EXPECT(fp8q_grouped_gemm(a, sa, nullptr, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP32, c, 4096,
-                           stream_tag()),
+  EXPECT(fp8q_grouped_gemm_ex(a, sa, offs, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_F32, FP8Q_ACC_FP8_MFMA, c, 4096,
+                              stream_tag()),
+         FP8Q_OK, true);
+  CHECK(last_is("grouped_gemm", {16, 8776, 4096, 7168, 0, FP8Q_ACC_FP8_MFMA, 4096}, {a, sa, offs, w, sw, c}));
+  EXPECT(fp8q_grouped_gemm_ex(a, sa, offs, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_F32, 7, c, 4096, stream_tag()),
          FP8Q_ERR_INVALID_ARG, false);
-  EXPECT(fp8q_grouped_gemm(a, sa, offs, -1, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP32, c, 4096,
-                           stream_tag()),
+  EXPECT(fp8q_grouped_gemm(a, sa, nullptr, 16, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, c, 4096, stream_tag()),
+         FP8Q_ERR_INVALID_ARG, false);
+  EXPECT(fp8q_grouped_gemm(a, sa, offs, -1, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, c, 4096, stream_tag()),
          FP8Q_ERR_INVALID_ARG, false);
   // G experts of N x K codes must stay below 2 GiB
-  EXPECT(fp8q_grouped_gemm(a, sa, offs, 80, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, FP8Q_ACC_FP32, c, 4096,
-                           stream_tag()),
+  EXPECT(fp8q_grouped_gemm(a, sa, offs, 80, 8776, w, sw, 4096, 7168, FP8Q_OUT_BF16, c, 4096, stream_tag()),
          FP8Q_ERR_SHAPE, false);
 
   auto* dw = addr<float>(9);
-  EXPECT(fp8q_wgrad(a, sa, w, sw, 2048, 7168, 16384, FP8Q_ACC_FP32, dw, 7168, stream_tag()), FP8Q_OK, true);
+  EXPECT(fp8q_wgrad(a, sa, w, sw, 2048, 7168, 16384, dw, 7168, stream_tag()), FP8Q_OK, true);
   CHECK(last_is("wgrad", {2048, 7168, 16384, FP8Q_ACC_FP32, 7168}, {a, sa, w, sw, dw}));
-  EXPECT(fp8q_wgrad(a, sa, w, sw, 2048, 7168, 16100, FP8Q_ACC_FP32, dw, 7168, stream_tag()), FP8Q_ERR_SHAPE, false);
+  EXPECT(fp8q_wgrad_ex(a, sa, w, sw, 2048, 7168, 16384, FP8Q_ACC_FP8_MFMA_SCALED, dw, 7168, stream_tag()), FP8Q_OK,
+         true);
+  CHECK(last_is("wgrad", {2048, 7168, 16384, FP8Q_ACC_FP8_MFMA_SCALED, 7168}, {a, sa, w, sw, dw}));
+  EXPECT(fp8q_wgrad_ex(a, sa, w, sw, 2048, 7168, 16384, -1, dw, 7168, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
+  EXPECT(fp8q_wgrad(a, sa, w, sw, 2048, 7168, 16100, dw, 7168, stream_tag()), FP8Q_ERR_SHAPE, false);
 }
 
 void moe_glue() {
@@ -342,6 +355,41 @@ void moe_glue() {
          FP8Q_ERR_SHAPE, false);
 }
 
+// The largest row counts the entry points accept reach the kernels' tile
+// sweeps: a tile index plus one stride of the sweep must stay below 2^32 (the
+// kernels count tiles in 32-bit unsigned), and the grid helpers must not
+// overflow.
+void large_sweeps() {
+  const void* x = addr<void>(1);
+  auto* codes = addr<uint8_t>(2);
+  auto* scales = addr<float>(3);
+  const int64_t rows = (int64_t(1) << 31) - (int64_t(1) << 25);
+  EXPECT(fp8q_quantize_act(x, rows, 1, 16, FP8Q_TILE_ROW, FP8Q_SCALE_FREE, codes, 16, scales, stream_tag()), FP8Q_OK,
+         true);
+  CHECK(last_is("quant_rows", {rows, 1, 16, 0, 16}, {x, codes, scales}));
+  EXPECT(fp8q_quantize_linear(x, rows, 1, 16, FP8Q_SCALE_POW2, codes, 16, scales, nullptr, 0, 16, FP8Q_SCALE_FREE,
+                              nullptr, 16, nullptr, stream_tag()),
+         FP8Q_OK, true);
+  EXPECT(fp8q_swiglu_quantize(x, rows, 1, 2, FP8Q_SCALE_FREE, codes, 16, scales, FP8Q_SCALE_FREE, nullptr, 0, nullptr,
+                              stream_tag()),
+         FP8Q_OK, true);
+  CHECK(last_is("swiglu_quant", {rows, 1, 2, 0, 16, 0, 0}, {x, codes, scales, nullptr, nullptr}));
+  // one tile more than the 32-bit signed range is refused
+  EXPECT(fp8q_quantize_act(x, int64_t(1) << 30, 257, 272, FP8Q_TILE_ROW, FP8Q_SCALE_FREE, codes, 272, scales,
+                           stream_tag()),
+         FP8Q_ERR_SHAPE, false);
+  for (int64_t ntiles : {int64_t(1), int64_t(63), int64_t(64), int64_t(1) << 26, rows, (int64_t(1) << 31) - 1}) {
+    const int g = fp8q::rows_grid(ntiles);
+    CHECK(g >= 1 && g <= fp8q::kMaxRowsGrid);
+    CHECK(int64_t(g) * 64 >= std::min<int64_t>(ntiles, int64_t(fp8q::kMaxRowsGrid) * 64));
+    const uint64_t stride = uint64_t(g) * 64;  // tiles per sweep of the whole grid
+    CHECK(uint64_t(ntiles - 1) + stride < (uint64_t(1) << 32));
+    const int sg = fp8q::stream_grid((ntiles + 3) / 4);
+    CHECK(sg >= 1 && sg <= fp8q::kMaxStreamGrid);
+    CHECK(uint64_t(ntiles - 1) + uint64_t(sg) * 16 < (uint64_t(1) << 32));
+  }
+}
+
 void status_strings() {
   for (int s = FP8Q_OK; s <= FP8Q_ERR_DEVICE; ++s) CHECK(std::strlen(fp8q_status_string((fp8q_status)s)) > 0);
   CHECK(std::strcmp(fp8q_status_string((fp8q_status)42), "unknown status") == 0);
@@ -354,6 +402,7 @@ int main() {
   quantizers();
   gemms();
   moe_glue();
+  large_sweeps();
   status_strings();
   if (g_failures) {
     std::printf("%d host ABI checks failed\n", g_failures);

@@ -75,17 +75,44 @@ def test_quantize_weight_validation(lib):
 
 
 def test_gemm_validation(lib):
+    # the section 8(b) prototype: (a, sa, w, sw, M, N, K, out_dtype, c, ld_c, stream)
     g = lib.fp8q_gemm
-    assert g(None, None, None, None, 0, 4, 128, 0, 0, None, 4, None) == fp8q.OK
-    assert g(P16, P16, P16, P16, 4, 4, 100, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE  # K % 128
-    assert g(P16, P16, P16, P16, 4, 4, 128, 2, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(None, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(P16, P16, P16, P16, 4, 8, 128, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE  # ld_c < N
-    assert g(P16, P16, P16, P16, 4, 4, 128, 1, 0, P8, 4, None) == fp8q.ERR_ALIGN
-    assert g(P16, P16, P8, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_ALIGN
-    assert g(P16, P16, P16, P16, 4, 4, -128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert g(P16, P16, P16, P16, 4, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
-    assert g(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(None, None, None, None, 0, 4, 128, 0, None, 4, None) == fp8q.OK
+    assert g(P16, P16, P16, P16, 4, 4, 100, 0, P16, 4, None) == fp8q.ERR_SHAPE  # K % 128
+    assert g(P16, P16, P16, P16, 4, 4, 128, 2, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(None, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert g(P16, P16, P16, P16, 4, 8, 128, 0, P16, 4, None) == fp8q.ERR_SHAPE  # ld_c < N
+    assert g(P16, P16, P16, P16, 4, 4, 128, 1, P8, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P8, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    assert g(P16, P16, P16, P16, 4, 4, -128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    # the _ex form takes acc after out_dtype
+    gx = lib.fp8q_gemm_ex
+    assert gx(None, None, None, None, 0, 4, 128, 0, 0, None, 4, None) == fp8q.OK
+    assert gx(P16, P16, P16, P16, 4, 4, 100, 0, 1, P16, 4, None) == fp8q.ERR_SHAPE
+    assert gx(P16, P16, P16, P16, 4, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert gx(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
+
+
+def test_section_8b_prototypes_in_header():
+    """fp8q_gemm, fp8q_grouped_gemm and fp8q_wgrad keep exactly the argument
+    lists of the boundary (no accumulation argument); the _ex forms add it."""
+    text = " ".join(open(HEADER).read().split())
+
+    def params(name):
+        m = re.search(r"fp8q_status " + name + r"\((.*?)\);", text)
+        assert m, name
+        return [p.strip().split()[-1].lstrip("*") for p in m.group(1).split(",")]
+
+    assert params("fp8q_gemm") == ["a", "a_scales", "w", "w_scales", "M", "N", "K", "out_dtype", "c", "ld_c",
+                                   "stream"]
+    assert params("fp8q_grouped_gemm") == ["a", "a_scales", "offsets", "G", "rows_cap", "w", "w_scales", "N", "K",
+                                           "out_dtype", "c", "ld_c", "stream"]
+    assert params("fp8q_wgrad") == ["dy_t", "dy_scales", "x_t", "x_scales", "Nout", "Kin", "T", "dw", "ld_dw",
+                                    "stream"]
+    assert params("fp8q_gemm_ex") == params("fp8q_gemm")[:8] + ["acc"] + params("fp8q_gemm")[8:]
+    assert params("fp8q_grouped_gemm_ex") == (params("fp8q_grouped_gemm")[:10] + ["acc"] +
+                                              params("fp8q_grouped_gemm")[10:])
+    assert params("fp8q_wgrad_ex") == params("fp8q_wgrad")[:7] + ["acc"] + params("fp8q_wgrad")[7:]
 
 
 def test_quantize_weight_t_validation(lib):
@@ -101,18 +128,22 @@ def test_quantize_weight_t_validation(lib):
 
 def test_grouped_and_wgrad_validation(lib):
     gg = lib.fp8q_grouped_gemm
-    assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.OK  # no groups
-    assert gg(P16, P16, P16, -1, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert gg(P16, P16, None, 2, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, 0, P16, 4, None) == fp8q.ERR_SHAPE
-    assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    assert gg(P16, P16, P16, 0, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.OK  # no groups
+    assert gg(P16, P16, P16, -1, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, None, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, P16, 4, None) == fp8q.ERR_SHAPE
+    assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
+    ggx = lib.fp8q_grouped_gemm_ex
+    assert ggx(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert ggx(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, 1, P16, 4, None) == fp8q.ERR_SHAPE
     wg = lib.fp8q_wgrad
-    assert wg(P16, P16, P16, P16, 0, 4, 128, 0, P16, 4, None) == fp8q.OK
-    assert wg(P16, P16, P16, P16, 4, 4, 200, 0, P16, 4, None) == fp8q.ERR_SHAPE
-    assert wg(P16, P16, P16, P16, 4, 8, 128, 0, P16, 4, None) == fp8q.ERR_SHAPE
-    assert wg(P16, None, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_INVALID_ARG
-    assert wg(P16, P16, P16, P16, 4, 4, 128, 5, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
-    assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    assert wg(P16, P16, P16, P16, 0, 4, 128, P16, 4, None) == fp8q.OK
+    assert wg(P16, P16, P16, P16, 4, 4, 200, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, P16, P16, P16, 4, 8, 128, P16, 4, None) == fp8q.ERR_SHAPE
+    assert wg(P16, None, P16, P16, 4, 4, 128, P16, 4, None) == fp8q.ERR_INVALID_ARG
+    wgx = lib.fp8q_wgrad_ex
+    assert wgx(P16, P16, P16, P16, 4, 4, 128, 5, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert wgx(P16, P16, P16, P16, 4, 4, 200, 2, P16, 4, None) == fp8q.ERR_SHAPE
 
 
 def test_quantize_linear_validation(lib):
@@ -181,12 +212,15 @@ def test_valid_calls_reach_the_device_check(lib):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
-    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 4, 128, 0, P16, 4, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_act(P16, 4, 8, 8, 0, 0, P16, 16, P16, None) == fp8q.ERR_DEVICE
     # leading dimensions need no alignment (unaligned strides take element-wise paths)
     assert lib.fp8q_quantize_act(P16, 4, 7, 7, 0, 0, P16, 7, P16, None) == fp8q.ERR_DEVICE
-    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 0, P16, 5, None) == fp8q.ERR_DEVICE
-    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm(P16, P16, P16, P16, 4, 5, 128, 1, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_gemm_ex(P16, P16, P16, P16, 4, 5, 128, 1, 1, P16, 5, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_grouped_gemm(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_wgrad(P16, P16, P16, P16, 4, 4, 128, P16, 4, None) == fp8q.ERR_DEVICE
+    assert lib.fp8q_wgrad_ex(P16, P16, P16, P16, 4, 4, 128, 2, P16, 4, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_weight_t(P16, 4, 8, 8, 0, None, 0, None, P16, 16, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_gemm_quantized(P16, P16, P16, P16, 4, 5, 128, 0, 1, P16, 5, P16, None) == fp8q.ERR_DEVICE
     assert lib.fp8q_quantize_linear(P16, 4, 100, 100, 0, P16, 100, P16, P16, 5, 100, 1, P16, 100, P16,

@@ -195,6 +195,31 @@ def test_grouped_moe_one_gpu_share_sampled():
             assert ok.all(), f"grouped {name} expert {gi}: {int((~ok).sum())} bad"
 
 
+def test_grouped_offsets_past_rows_cap_are_clamped():
+    """A routing table whose last offset runs past rows_cap: the kernel clamps
+    each group's rows to [0, rows_cap], so the groups inside are computed as
+    usual, the one that straddles rows_cap is cut there, and nothing is read
+    or written beyond rows_cap (guard rows of the output stay NaN)."""
+    d, cases = _grouped_case(tokens=256, hidden=256, inter=128, with_down=False)
+    _, _, wc, ws = cases[0]
+    g, n, k = wc.shape[0], wc.shape[1], wc.shape[2]
+    rows_cap = 300
+    bounds = [0, 100, 250] + [400] * (g - 2)  # offsets[G] = 400 > rows_cap
+    offs = np.array(bounds, dtype=np.int32)
+    rng = np.random.default_rng(5)
+    a_bits = synth.bf16_rne(rng.standard_normal((rows_cap, k)).astype(np.float32))
+    a_c, a_s = Q.quantize_rows(a_bits)
+    say(f"[gemm] grouped, offsets {bounds[:4]}... past rows_cap={rows_cap}")
+    full = torch.full((rows_cap + 64, n), float("nan"), dtype=torch.float32, device="cuda:0")
+    fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out=full[:rows_cap])
+    got = host(full)
+    assert np.isnan(got[rows_cap:]).all(), "rows beyond rows_cap were written"
+    for gi, (lo, hi) in enumerate([(0, 100), (100, 250), (250, rows_cap)]):
+        ref, s = G.gemm(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi])
+        ok = G.accept_f32(got[lo:hi].astype(np.float64), ref, s)
+        assert ok.all(), f"group {gi}: {int((~ok).sum())} bad"
+
+
 def test_grouped_equals_dense_per_group():
     d, cases = _grouped_case(tokens=256, hidden=256, inter=128, with_down=False)
     a_c, a_s, wc, ws = cases[0]
