@@ -4,24 +4,32 @@ One step = one pass of the path over the dense expert up-projection
 (A BF16 4096 x 7168 with 0.1% outliers x100, W BF16 4096 x 7168 ~N(0, 0.02)):
 1x128 online max-abs quantization of A and 128x128 quantization of W (one
 launch, fp8q_quantize_linear), then the block-scaled FP8 GEMM to BF16
-C[4096, 4096] -- all in libfp8q.so.
-Inputs are generated on the host (seeded), copied to HBM once, and are
-resident before the timed region starts.
+C[4096, 4096] (fp8q_gemm) -- all in libfp8q.so.  Inputs are generated on the
+host (seeded), copied to HBM once, and are resident before the timed region
+starts.
 
-Prints one JSON line:
-  value      = whole-step throughput, 2*M*N*K / step time (TFLOP/s)
-  kernels    = per-kernel average durations from HIP events on the launch
-               stream around --steps back-to-back launches of that kernel,
-               with GB/s or TFLOP/s and the fraction of the MI355X roofline
-  *_after_cache_flush = the step's GEMM and quantizer as single launches,
-               each after a 1 GiB write that evicts the caches (median, min)
-  roofline   = the dominant kernel (the GEMM) against the dense FP8 MFMA peak
-  cpu_baseline = the oracle timed on the host on a bounded sample
+Timing:
+  * before the --warmup untimed steps, the step runs for PREWARM_MS more
+    (untimed), so the timed region sees the GPU's steady clock whatever
+    --warmup is;
+  * the timed region is exactly --steps steps between two synchronizations;
+    inside it, HIP events on the launch stream bracket every GEMM launch,
+    which gives the GEMM's live average duration (the roofline's `achieved`);
+  * every other kernel figure is the median of per-launch HIP event
+    durations after a time-based warm-up of that kernel (>= WARM_MS), so it
+    does not depend on what ran before it; quantizers rotate over copies of
+    their inputs larger than the 256 MB Infinity Cache; `after_cache_flush`
+    figures write 1 GiB before each launch.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 400] [--no-cpu-baseline]
+Prints one JSON line (contract fields first; `configs` holds every workload
+of the five configurations; `cpu_baseline` times the oracle on the host and
+checks a sample of the timed step's outputs against it).
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,31 +43,41 @@ sys.path.insert(0, ROOT)
 M, N, K = 4096, 4096, 7168
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
 METRIC = "block-scaled FP8 GEMM TFLOP/s + quantize GB/s, % of MI355X roofline"
+PREWARM_MS = 300.0
+WARM_MS = 100.0
 
 # algorithmic bytes: BF16 read + code write + one float32 scale per tile
 ACT_BYTES = M * K * 2 + M * K + M * (K // 128) * 4
 WGT_BYTES = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
 GEMM_FLOP = 2.0 * M * N * K
-# HBM traffic of one dense GEMM launch (acc=FP32) from rocprofv3 counters
-# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, calibrated on a 256 MiB copy) for
-# the kernel as it stands; None until re-measured after a kernel change
-GEMM_TRAFFIC_BYTES = 217_230_000
+# codes and scales read once, BF16 C written once
+GEMM_MIN_BYTES = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 4 + M * N * 2
+
+# HBM traffic of one dense-GEMM launch from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE; each scaled by what the counter reads for a plain
+# copy of known size), valid only for the kernel source it was measured on:
+# when csrc/gemm.hip no longer hashes to `source_sha256` the bench reports
+# traffic null.
+GEMM_TRAFFIC = {"bytes": None, "source_sha256": None, "profile": None}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    # the GPU needs tens of milliseconds of load to reach its steady clock:
-    # the default warm-up (400 steps, ~90 ms, untimed) runs past that ramp,
-    # and the timed region is 200 steps (~45 ms)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 256 MiB device-to-device copy (torch) --steps times; used to "
                         "scale the FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run")
     return p.parse_args()
+
+
+def source_sha256(name):
+    with open(os.path.join(ROOT, "fine_grained_fp8_fp8q_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def copy_calibration(steps):
@@ -80,331 +98,447 @@ def copy_calibration(steps):
                       "GB/s": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline():
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    quantize 1024 rows of A and 1024 rows of W, then the block-scaled GEMM of
-    those rows (1024 x 1024 x 7168).  Rate = GEMM FLOPs / total time."""
-    import threadpoolctl
-    from oracle import gemm as G, quantize as Q
-    import synth
-    d = synth.dense_up()
-    rows = 1024
-    a, w = np.ascontiguousarray(d["a"][:rows]), np.ascontiguousarray(d["w"][:rows])
-    t0 = time.perf_counter()
-    a_c, a_s = Q.quantize_rows(a)
-    w_c, w_s = Q.quantize_blocks(w)
-    t1 = time.perf_counter()
-    G.gemm(a_c, a_s, w_c, w_s)
-    t2 = time.perf_counter()
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    flop = 2.0 * rows * rows * K
-    return {"value": flop / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"A rows 0..{rows - 1} and W rows 0..{rows - 1} of the 4096x4096x7168 workload: "
-                      f"quantize ({t1 - t0:.2f} s) + GEMM {rows}x{rows}x{K} ({t2 - t1:.2f} s), "
-                      f"rate = GEMM FLOPs / total"}
+# ------------------------------------------------------------ timing ----
+
+class Clock:
+    """HIP-event timing on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+        self._scratch = None
+
+    def _ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def warm(self, fn, ms=WARM_MS):
+        """Launch fn(i) back to back for at least `ms` milliseconds."""
+        t0 = time.perf_counter()
+        i = 0
+        while True:
+            for _ in range(8):
+                if fn(i) != 0:
+                    raise RuntimeError("fp8q call failed")
+                i += 1
+            self.torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                return
+
+    def launches(self, fn, reps, flush=False):
+        """Per-launch durations (us) of fn(0..reps-1): back to back, one event
+        between consecutive launches; with flush=True each launch follows a
+        1 GiB write and has its own event pair."""
+        if not flush:
+            ev = [self._ev() for _ in range(reps + 1)]
+            ev[0].record(self.stream)
+            for i in range(reps):
+                if fn(i) != 0:
+                    raise RuntimeError("fp8q call failed")
+                ev[i + 1].record(self.stream)
+            ev[-1].synchronize()
+            return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+        if self._scratch is None:
+            self._scratch = self.torch.empty(1 << 30, dtype=self.torch.uint8, device="cuda:0")
+        out = []
+        for i in range(reps):
+            self._scratch.fill_(i & 0xFF)
+            e0, e1 = self._ev(), self._ev()
+            e0.record(self.stream)
+            if fn(i) != 0:
+                raise RuntimeError("fp8q call failed")
+            e1.record(self.stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3)
+        return out
+
+    def stats(self, fn, reps, flop=None, nbytes=None, flush=False, warm=True):
+        if warm:
+            self.warm(fn)
+        t = self.launches(fn, reps, flush)
+        med = float(np.median(t))
+        r = {"median_us": round(med, 2), "min_us": round(float(np.min(t)), 2), "launches": reps}
+        if flop is not None:
+            r["TFLOP/s"] = round(flop / med / 1e6, 1)
+            r["frac_fp8_peak"] = round(flop / med / 1e6 / FP8_PEAK_TFLOPS, 4)
+        if nbytes is not None:
+            r["GB/s"] = round(nbytes / med / 1e3, 1)
+            r["frac_hbm"] = round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4)
+            r["bytes"] = int(nbytes)
+        return r
+
+    def after_idle(self, fn, reps=20):
+        """Median of the first `reps` launches after 200 ms without GPU work
+        (the HBM-bound kernels run faster in the first ~1.5 ms of load)."""
+        self.torch.cuda.synchronize()
+        time.sleep(0.2)
+        return float(np.median(self.launches(fn, reps)))
+
+    def release(self):
+        self._scratch = None
 
 
-def quantize_only_rates(torch, fp8q, lib, stream, reps):
-    """Quantizer bandwidth at the quantize-only sizes: activations 16384 x 7168
-    (standard Student-t(3)) in free and power-of-two modes, weights 7168 x 18432
-    (~N(0, 0.02)).  HIP events around `reps` launches alternating over two
-    input/output sets (each set is larger than the Infinity Cache)."""
-    import synth
-    dev = torch.device("cuda:0")
-    out = {}
-    act = synth.quant_only_act()
-    rows, cols = act.shape
-    xs = [torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).to(dev)]
-    xs.append(xs[0].clone())
-    cs = [torch.empty((rows, cols), dtype=torch.uint8, device=dev) for _ in range(2)]
-    ss = torch.empty((rows, cols // 128), dtype=torch.float32, device=dev)
-    abytes = rows * cols * 3 + rows * (cols // 128) * 4
-    for mode_name, mode in (("free", fp8q.SCALE_FREE), ("pow2", fp8q.SCALE_POW2)):
-        def fn(i):
-            return lib.fp8q_quantize_act(xs[i & 1].data_ptr(), rows, cols, cols, fp8q.TILE_ROW, mode,
-                                         cs[i & 1].data_ptr(), cols, ss.data_ptr(), stream.cuda_stream)
-        burst = _burst_us(torch, stream, fn)
-        us = _event_us(torch, stream, fn, reps)
-        out[f"act_16384x7168_{mode_name}"] = {"us": round(us, 2), "GB/s": round(abytes / us / 1e3, 1),
-                                              "frac_hbm": round(abytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                                              "bytes": abytes, "us_first_20_after_idle": round(burst, 2),
-                                              "frac_hbm_first_20_after_idle":
-                                                  round(abytes / burst / 1e3 / HBM_PEAK_GBS, 4)}
-    del xs, cs, ss
-    wt = synth.quant_only_weight()
-    n, k = wt.shape
-    ws = [torch.from_numpy(wt.view(np.int16)).view(torch.bfloat16).to(dev)]
-    ws.append(ws[0].clone())
-    cs = [torch.empty((n, k), dtype=torch.uint8, device=dev) for _ in range(2)]
-    ss = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
-    wbytes = n * k * 3 + (n // 128) * (k // 128) * 4
-
-    def fw(i):
-        return lib.fp8q_quantize_weight(ws[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, cs[i & 1].data_ptr(),
-                                        k, ss.data_ptr(), stream.cuda_stream)
-    burst = _burst_us(torch, stream, fw)
-    us = _event_us(torch, stream, fw, reps)
-    out["weight_7168x18432"] = {"us": round(us, 2), "GB/s": round(wbytes / us / 1e3, 1),
-                                "frac_hbm": round(wbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": wbytes,
-                                "us_first_20_after_idle": round(burst, 2),
-                                "frac_hbm_first_20_after_idle": round(wbytes / burst / 1e3 / HBM_PEAK_GBS, 4)}
-    return out
-
-
-def _roofline(flop, nbytes, us):
+def roofline_entry(flop, nbytes, med_us):
     """Time at the roofline max(flop / FP8 peak, bytes / HBM peak) and the
-    fraction of it reached in `us`."""
+    fraction of it reached in med_us."""
     t = max(flop / (FP8_PEAK_TFLOPS * 1e6), nbytes / (HBM_PEAK_GBS * 1e3))
-    return {"us": round(us, 2), "TFLOP/s": round(flop / us / 1e6, 1), "GB/s": round(nbytes / us / 1e3, 1),
-            "flop": flop, "bytes": nbytes, "roofline_us": round(t, 2), "frac_roofline": round(t / us, 4),
+    return {"roofline_us": round(t, 2), "frac_roofline": round(t / med_us, 4),
             "bound": "mfma" if flop / (FP8_PEAK_TFLOPS * 1e6) >= nbytes / (HBM_PEAK_GBS * 1e3) else "hbm"}
 
 
-def moe_rates(torch, fp8q, lib, stream, reps):
-    """One GPU's share of the MoE layer: 8192 tokens routed top-8 over 256
-    experts (Zipf(1.1) popularity), 16 hosted experts, one of them empty.
-    Tokens are quantized once (1x128), then their codes and scales are
-    gathered by expert (FP8 dispatch gather); grouped up-projection
-    7168 -> 4096 and grouped down-projection 2048 -> 7168, BF16 out; the
-    SwiGLU between them fused with the 1x128 quantization of its output; and
-    the whole expert FFN forward (gather, up, SwiGLU + quantize, down) as one
-    timed pass."""
+# -------------------------------------------------------- workloads ----
+
+def bf16_dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def tiny_linear(torch, fp8q, lib, clock, sp):
+    """Config 1, 128 x 256 x 512, FP32 out: latency of one pass (quantize A and
+    W in one launch, then the GEMM), and of each kernel."""
     import synth
-    dev = torch.device("cuda:0")
+    d = synth.tiny_linear()
+    a, w = bf16_dev(torch, d["a"]), bf16_dev(torch, d["w"])
+    m, k = a.shape
+    n = w.shape[0]
+    ac, as_, wc, ws = fp8q.quantize_linear(a, w)
+    c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
+
+    def q(i):
+        return lib.fp8q_quantize_linear(a.data_ptr(), m, k, k, fp8q.SCALE_FREE, ac.data_ptr(), ac.stride(0),
+                                        as_.data_ptr(), w.data_ptr(), n, k, fp8q.SCALE_FREE, wc.data_ptr(),
+                                        wc.stride(0), ws.data_ptr(), sp)
+
+    def g(i):
+        return lib.fp8q_gemm(ac.data_ptr(), as_.data_ptr(), wc.data_ptr(), ws.data_ptr(), m, n, k, fp8q.OUT_F32,
+                             c.data_ptr(), n, sp)
+
+    def step(i):
+        return q(i) or g(i)
+    return {"workload": "tiny linear: quantize A 128x512 (1x128) + W 256x512 (128x128), GEMM -> FP32 [128, 256]",
+            "step_latency": clock.stats(step, 200), "quantize_linear": clock.stats(q, 200),
+            "gemm": clock.stats(g, 200, flop=2.0 * m * n * k)}
+
+
+def quantize_only(torch, fp8q, lib, clock, sp, reps):
+    """Config 3: activations 16384 x 7168 (Student-t(3)) in both scale modes,
+    weights 7168 x 18432 per 128 x 128 block; two input/output sets, each
+    larger than the Infinity Cache, alternate."""
+    import synth
+    out = {}
+    act = synth.quant_only_act()
+    rows, cols = act.shape
+    xs = [bf16_dev(torch, act)]
+    xs.append(xs[0].clone())
+    cs = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    ss = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda:0")
+    abytes = rows * cols * 3 + rows * (cols // 128) * 4
+    for mode_name, mode in (("free", fp8q.SCALE_FREE), ("pow2", fp8q.SCALE_POW2)):
+        def fn(i, mode=mode):
+            return lib.fp8q_quantize_act(xs[i & 1].data_ptr(), rows, cols, cols, fp8q.TILE_ROW, mode,
+                                         cs[i & 1].data_ptr(), cols, ss.data_ptr(), sp)
+        r = clock.stats(fn, reps, nbytes=abytes)
+        r["median_us_first_20_after_idle"] = round(clock.after_idle(fn), 2)
+        out[f"act_16384x7168_{mode_name}"] = r
+    del xs, cs, ss
+    wt = synth.quant_only_weight()
+    n, k = wt.shape
+    ws = [bf16_dev(torch, wt)]
+    ws.append(ws[0].clone())
+    cs = [torch.empty((n, k), dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    ss = torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda:0")
+    wbytes = n * k * 3 + (n // 128) * (k // 128) * 4
+
+    def fw(i):
+        return lib.fp8q_quantize_weight(ws[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, cs[i & 1].data_ptr(), k,
+                                        ss.data_ptr(), sp)
+    r = clock.stats(fw, reps, nbytes=wbytes)
+    r["median_us_first_20_after_idle"] = round(clock.after_idle(fw), 2)
+    out["weight_7168x18432"] = r
+    return out
+
+
+def moe(torch, fp8q, lib, clock, sp, reps):
+    """Config 4, one GPU's share of the MoE layer: 8192 tokens routed top-8
+    over 256 experts (Zipf(1.1) popularity), 16 hosted experts (one empty).
+    Tokens are quantized once (1x128), their codes and scales gathered by
+    expert (FP8 dispatch gather); grouped up-projection 7168 -> 4096 and
+    down-projection 2048 -> 7168, BF16 out; SwiGLU fused with the 1x128
+    quantization of its output; the whole expert FFN forward as one pass."""
+    import synth
     d = synth.moe_grouped()
     G = len(d["counts"])
     rows = int(d["counts"].sum())
-    K_UP = d["x"].shape[1]
-
-    def bf(x):
-        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    x = bf(d["x"])
+    k_up = d["x"].shape[1]
+    x = bf16_dev(torch, d["x"])
     xq, xs = fp8q.quantize_act(x)
-    gather = torch.from_numpy(d["gather"].astype(np.int32)).to(dev)
+    gather = torch.from_numpy(d["gather"].astype(np.int32)).to("cuda:0")
     a_up, s_up = fp8q.gather_rows(xq, xs, gather)
-    off = torch.from_numpy(d["offsets"]).to(dev)
-    hq, hs = fp8q.quantize_act(bf(d["h"]))
+    off = torch.from_numpy(d["offsets"]).to("cuda:0")
+    hq, hs = fp8q.quantize_act(bf16_dev(torch, d["h"]))
     out = {"experts": G, "rows_per_expert": [int(v) for v in d["counts"]], "rows": rows}
 
-    # FP8 dispatch gather of the hosted rows; the timing rotates over five
-    # copies of the quantized tokens (more than the 256 MB Infinity Cache)
-    nb_up = K_UP // 128
-    srcs = [(xq, xs)] + [fp8q.quantize_act(x) for _ in range(4)]
-
-    def fg_from(i):
-        q, sc = srcs[i % len(srcs)]
-        return lib.fp8q_gather_rows(q.data_ptr(), q.shape[0], K_UP, q.stride(0), sc.data_ptr(),
-                                    gather.data_ptr(), rows, a_up.data_ptr(), a_up.stride(0), s_up.data_ptr(),
-                                    stream.cuda_stream)
-    us = _event_us(torch, stream, fg_from, reps)
-    del srcs
+    nb_up = k_up // 128
+    srcs = [(xq, xs)] + [fp8q.quantize_act(x) for _ in range(4)]  # > Infinity Cache in rotation
 
     def fg(i):
-        return lib.fp8q_gather_rows(xq.data_ptr(), xq.shape[0], K_UP, xq.stride(0), xs.data_ptr(),
-                                    gather.data_ptr(), rows, a_up.data_ptr(), a_up.stride(0), s_up.data_ptr(),
-                                    stream.cuda_stream)
-    gbytes = 2 * rows * (K_UP + nb_up * 4) + rows * 4
-    out["dispatch_gather_fp8"] = {"us": round(us, 2), "GB/s": round(gbytes / us / 1e3, 1),
-                                  "frac_hbm": round(gbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": gbytes}
+        q, sc = srcs[i % len(srcs)]
+        return lib.fp8q_gather_rows(q.data_ptr(), q.shape[0], k_up, q.stride(0), sc.data_ptr(), gather.data_ptr(),
+                                    rows, a_up.data_ptr(), a_up.stride(0), s_up.data_ptr(), sp)
+    gbytes = 2 * rows * (k_up + nb_up * 4) + rows * 4
+    out["dispatch_gather_fp8"] = clock.stats(fg, reps, nbytes=gbytes)
 
-    # SwiGLU + 1x128 quantization of the up-projection output shape, inputs
-    # rotated over ten copies (more than the Infinity Cache)
     inter = d["w_down"].shape[2]
-    sx0 = bf(synth.swiglu_input(rows=rows, inter=inter))
+    sx0 = bf16_dev(torch, synth.swiglu_input(rows=rows, inter=inter))
     sxs = [sx0] + [sx0.clone() for _ in range(9)]
-    sq = torch.empty((rows, inter), dtype=torch.uint8, device=dev)
-    ss = torch.empty((rows, inter // 128), dtype=torch.float32, device=dev)
-    cq = torch.empty((rows, 2 * inter), dtype=torch.uint8, device=dev)
-    cs = torch.empty((rows, 2 * inter // 128), dtype=torch.float32, device=dev)
+    sq = torch.empty((rows, inter), dtype=torch.uint8, device="cuda:0")
+    ssc = torch.empty((rows, inter // 128), dtype=torch.float32, device="cuda:0")
+    cq = torch.empty((rows, 2 * inter), dtype=torch.uint8, device="cuda:0")
+    cs = torch.empty((rows, 2 * inter // 128), dtype=torch.float32, device="cuda:0")
     for name, cache in (("swiglu_quantize", False), ("swiglu_quantize_with_pow2_cache", True)):
         def fs(i, cache=cache):
             return lib.fp8q_swiglu_quantize(sxs[i % len(sxs)].data_ptr(), rows, inter, 2 * inter, fp8q.SCALE_FREE,
-                                            sq.data_ptr(), inter, ss.data_ptr(), fp8q.SCALE_POW2,
+                                            sq.data_ptr(), inter, ssc.data_ptr(), fp8q.SCALE_POW2,
                                             cq.data_ptr() if cache else None, 2 * inter,
-                                            cs.data_ptr() if cache else None, stream.cuda_stream)
-        us = _event_us(torch, stream, fs, reps)
+                                            cs.data_ptr() if cache else None, sp)
         sbytes = rows * 2 * inter * 2 + rows * inter + rows * (inter // 128) * 4
         if cache:
             sbytes += rows * 2 * inter + rows * (2 * inter // 128) * 4
-        out[name] = {"us": round(us, 2), "GB/s": round(sbytes / us / 1e3, 1),
-                     "frac_hbm": round(sbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes": sbytes}
+        out[name] = clock.stats(fs, reps, nbytes=sbytes)
     del sxs, sx0, cq, cs
 
     weights = {}
     for name, wname, in_a, in_s in (("up_7168x4096", "w_up", a_up, s_up), ("down_2048x7168", "w_down", hq, hs)):
-        wb = bf(d[wname])
+        wb = bf16_dev(torch, d[wname])
         g, n, k = wb.shape
-        wq, ws = fp8q.quantize_weight(wb.view(g * n, k))
+        wq, wsc = fp8q.quantize_weight(wb.view(g * n, k))
         del wb
-        weights[wname] = (wq, ws, n, k)
-        c = torch.empty((rows, n), dtype=torch.bfloat16, device=dev)
+        weights[wname] = (wq, wsc, n, k)
+        c = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda:0")
+        flop = 2.0 * rows * n * k
+        nbytes = G * n * k + (G * n // 128) * (k // 128) * 4 + rows * k + rows * (k // 128) * 4 + rows * n * 2
+        per = 0.0  # sum of each expert's own roofline time
+        for m in d["counts"]:
+            if m:
+                per += max(2.0 * int(m) * n * k / (FP8_PEAK_TFLOPS * 1e6),
+                           (n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2))
+                           / (HBM_PEAK_GBS * 1e3))
         for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
-            out[name + acc_name] = _grouped_rate(torch, lib, stream, reps, d["counts"], in_a, in_s, off, G, rows,
-                                                 wq, ws, n, k, c, acc, fp8q)
+            def fn(i, acc=acc, in_a=in_a, in_s=in_s, wq=wq, wsc=wsc, n=n, k=k, c=c):
+                return lib.fp8q_grouped_gemm_ex(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
+                                                wq.data_ptr(), wsc.data_ptr(), n, k, fp8q.OUT_BF16, acc,
+                                                c.data_ptr(), n, sp)
+            r = clock.stats(fn, reps, flop=flop, nbytes=nbytes)
+            r.update(roofline_entry(flop, nbytes, r["median_us"]))
+            r["per_expert_roofline_us"] = round(per, 2)
+            out[name + acc_name] = r
         del c
 
-    # expert FFN forward, default accumulation: dispatch gather -> up ->
-    # SwiGLU + quantize -> down
     wq_u, ws_u, n_u, k_u = weights["w_up"]
     wq_d, ws_d, n_d, k_d = weights["w_down"]
-    up_out = torch.empty((rows, n_u), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((rows, n_d), dtype=torch.bfloat16, device=dev)
+    up_out = torch.empty((rows, n_u), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty((rows, n_d), dtype=torch.bfloat16, device="cuda:0")
 
     def ffn(i):
         st = fg(i)
-        st = st or lib.fp8q_grouped_gemm_ex(a_up.data_ptr(), s_up.data_ptr(), off.data_ptr(), G, rows,
-                                         wq_u.data_ptr(), ws_u.data_ptr(), n_u, k_u, fp8q.OUT_BF16,
-                                         fp8q.ACC_FP32, up_out.data_ptr(), n_u, stream.cuda_stream)
-        st = st or lib.fp8q_swiglu_quantize(up_out.data_ptr(), rows, inter, n_u, fp8q.SCALE_FREE,
-                                            sq.data_ptr(), inter, ss.data_ptr(), fp8q.SCALE_POW2, None, 0,
-                                            None, stream.cuda_stream)
-        st = st or lib.fp8q_grouped_gemm_ex(sq.data_ptr(), ss.data_ptr(), off.data_ptr(), G, rows,
-                                         wq_d.data_ptr(), ws_d.data_ptr(), n_d, k_d, fp8q.OUT_BF16,
-                                         fp8q.ACC_FP32, y.data_ptr(), n_d, stream.cuda_stream)
+        st = st or lib.fp8q_grouped_gemm(a_up.data_ptr(), s_up.data_ptr(), off.data_ptr(), G, rows, wq_u.data_ptr(),
+                                         ws_u.data_ptr(), n_u, k_u, fp8q.OUT_BF16, up_out.data_ptr(), n_u, sp)
+        st = st or lib.fp8q_swiglu_quantize(up_out.data_ptr(), rows, inter, n_u, fp8q.SCALE_FREE, sq.data_ptr(),
+                                            inter, ssc.data_ptr(), fp8q.SCALE_POW2, None, 0, None, sp)
+        st = st or lib.fp8q_grouped_gemm(sq.data_ptr(), ssc.data_ptr(), off.data_ptr(), G, rows, wq_d.data_ptr(),
+                                         ws_d.data_ptr(), n_d, k_d, fp8q.OUT_BF16, y.data_ptr(), n_d, sp)
         return st
-    us = _event_us(torch, stream, ffn, reps)
     flop = 2.0 * rows * (n_u * k_u + n_d * k_d)
-    out["expert_ffn_forward"] = {"us": round(us, 2), "TFLOP/s": round(flop / us / 1e6, 1), "flop": flop,
-                                 "steps": "dispatch gather, grouped up GEMM, SwiGLU + quantize, grouped down GEMM"}
+    r = clock.stats(ffn, reps, flop=flop)
+    r["steps"] = "dispatch gather, grouped up GEMM, SwiGLU + quantize, grouped down GEMM"
+    out["expert_ffn_forward"] = r
     return out
 
 
-def _grouped_rate(torch, lib, stream, reps, counts, in_a, in_s, off, G, rows, wq, ws, n, k, c, acc, fp8q):
-    """Grouped GEMM time for one accumulation mode, with the whole-kernel and
-    the per-expert roofline."""
-    def fn(i):
-        return lib.fp8q_grouped_gemm_ex(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
-                                     wq.data_ptr(), ws.data_ptr(), n, k, fp8q.OUT_BF16, acc, c.data_ptr(),
-                                     n, stream.cuda_stream)
-    us = _event_us(torch, stream, fn, reps)
-    flop = 2.0 * rows * n * k
-    nbytes = G * n * k + (G * n // 128) * (k // 128) * 4 + rows * k + rows * (k // 128) * 4 + rows * n * 2
-    r = _roofline(flop, nbytes, us)
-    # sum over experts of each expert's own roofline time (a small
-    # expert is bound by reading its weights)
-    per = 0.0
-    for m in counts:
-        fe = 2.0 * int(m) * n * k
-        be = n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2)
-        per += max(fe / (FP8_PEAK_TFLOPS * 1e6), be / (HBM_PEAK_GBS * 1e3)) if m else 0.0
-    r["per_expert_roofline_us"] = round(per, 2)
-    return r
-
-
-def wgrad_rates(torch, fp8q, lib, stream, reps):
-    """Weight gradient over 16384 tokens: dY 16384 x 2048 and X 16384 x 7168
-    (BF16 ~N(0,1)) quantized in 128-token x 1-feature tiles (codes written
-    feature-major), then dW[2048, 7168] = dY^T X in FP32."""
+def wgrad(torch, fp8q, lib, clock, sp, reps):
+    """Config 5: dY 16384 x 2048 and X 16384 x 7168 (BF16 ~N(0,1)) quantized
+    in 128-token x 1-feature tiles (codes feature-major), then
+    dW[2048, 7168] = dY^T X in FP32."""
     import synth
-    dev = torch.device("cuda:0")
     d = synth.wgrad()
     out = {}
     q = {}
     for name, arr in (("dy", d["dy"]), ("x", d["x"])):
-        t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).to(dev)
+        t = bf16_dev(torch, arr)
         tok, feat = t.shape
-        codes = torch.empty((feat, tok), dtype=torch.uint8, device=dev)
-        scales = torch.empty((feat, tok // 128), dtype=torch.float32, device=dev)
+        codes = torch.empty((feat, tok), dtype=torch.uint8, device="cuda:0")
+        scales = torch.empty((feat, tok // 128), dtype=torch.float32, device="cuda:0")
+        t2 = t.clone()
 
-        def fn(i, t=t, tok=tok, feat=feat, codes=codes, scales=scales):
-            return lib.fp8q_quantize_act(t.data_ptr(), tok, feat, feat, fp8q.TILE_TOKEN_T, fp8q.SCALE_FREE,
-                                         codes.data_ptr(), tok, scales.data_ptr(), stream.cuda_stream)
-        us = _event_us(torch, stream, fn, reps)
+        def fn(i, ts=(t, t2), tok=tok, feat=feat, codes=codes, scales=scales):
+            return lib.fp8q_quantize_act(ts[i & 1].data_ptr(), tok, feat, feat, fp8q.TILE_TOKEN_T, fp8q.SCALE_FREE,
+                                         codes.data_ptr(), tok, scales.data_ptr(), sp)
         nbytes = tok * feat * 3 + feat * (tok // 128) * 4
-        out[f"quantize_{name}_token_t_{tok}x{feat}"] = {"us": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
-                                                        "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                                                        "bytes": nbytes}
+        out[f"quantize_{name}_token_t_{tok}x{feat}"] = clock.stats(fn, reps, nbytes=nbytes)
+        fn(0)
         q[name] = (codes, scales, tok, feat)
-        del t
+        del t, t2
     dyc, dys, T, nout = q["dy"]
     xc, xs, _, kin = q["x"]
-    dw = torch.empty((nout, kin), dtype=torch.float32, device=dev)
-
+    dw = torch.empty((nout, kin), dtype=torch.float32, device="cuda:0")
     flop = 2.0 * nout * kin * T
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
     for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
         def fg(i, acc=acc):
-            return lib.fp8q_wgrad_ex(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T,
-                                  acc, dw.data_ptr(), kin, stream.cuda_stream)
-        us = _event_us(torch, stream, fg, reps)
-        out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = _roofline(flop, nbytes, us)
+            return lib.fp8q_wgrad_ex(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T, acc,
+                                     dw.data_ptr(), kin, sp)
+        r = clock.stats(fg, reps, flop=flop, nbytes=nbytes)
+        r.update(roofline_entry(flop, nbytes, r["median_us"]))
+        out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = r
     return out
 
 
-def dgrad_rates(torch, fp8q, lib, stream, reps, w):
-    """Activation gradient of the up-projection: the weight W [4096, 7168]
-    quantized once into both orientations (one read, two code copies), then
-    dX [4096, 7168] = dY [4096, 4096] . W (reduction over N = 4096), dY
-    BF16 ~N(0,1) quantized in 1x128 tiles along N, BF16 out."""
+def dgrad(torch, fp8q, lib, clock, sp, reps, w):
+    """Activation gradient of the up-projection: W [4096, 7168] quantized once
+    into both orientations, then dX [4096, 7168] = dY [4096, 4096] . W
+    (reduction over N = 4096), dY BF16 ~N(0,1) in 1x128 tiles along N."""
     import synth
-    dev = torch.device("cuda:0")
     n, k = w.shape
     m = 4096
-    codes = torch.empty((n, k), dtype=torch.uint8, device=dev)
-    scales = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
-    codes_t = torch.empty((k, n), dtype=torch.uint8, device=dev)
-    scales_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
+    codes = torch.empty((n, k), dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda:0")
+    codes_t = torch.empty((k, n), dtype=torch.uint8, device="cuda:0")
+    scales_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device="cuda:0")
     w2 = [w, w.clone()]
 
     def fq(i):
         return lib.fp8q_quantize_weight_t(w2[i & 1].data_ptr(), n, k, k, fp8q.SCALE_FREE, codes.data_ptr(), k,
-                                          scales.data_ptr(), codes_t.data_ptr(), n, scales_t.data_ptr(),
-                                          stream.cuda_stream)
-    us_q = _event_us(torch, stream, fq, reps)
+                                          scales.data_ptr(), codes_t.data_ptr(), n, scales_t.data_ptr(), sp)
     qbytes = n * k * 4 + 2 * (n // 128) * (k // 128) * 4
-    out = {"quantize_weight_both_orientations_4096x7168": {
-        "us": round(us_q, 2), "GB/s": round(qbytes / us_q / 1e3, 1),
-        "frac_hbm": round(qbytes / us_q / 1e3 / HBM_PEAK_GBS, 4), "bytes": qbytes}}
+    out = {"quantize_weight_both_orientations_4096x7168": clock.stats(fq, reps, nbytes=qbytes)}
     rng = np.random.default_rng(21)
-    dy = torch.from_numpy(synth.bf16_rne(rng.standard_normal((m, n)).astype(np.float32)).view(np.int16))
-    dyq, dys = fp8q.quantize_act(dy.view(torch.bfloat16).to(dev))
-    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    dy = bf16_dev(torch, synth.bf16_rne(rng.standard_normal((m, n)).astype(np.float32)))
+    dyq, dys = fp8q.quantize_act(dy)
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda:0")
     flop = 2.0 * m * n * k
     nbytes = m * n + n * k + m * (n // 128) * 4 + (k // 128) * (n // 128) * 4 + m * k * 2
     for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
         def fg(i, acc=acc):
-            return lib.fp8q_gemm_ex(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k,
-                                 n, fp8q.OUT_BF16, acc, dx.data_ptr(), k, stream.cuda_stream)
-        out[f"dgrad_{m}x{k}x{n}{acc_name}"] = _roofline(flop, nbytes, _event_us(torch, stream, fg, reps))
+            return lib.fp8q_gemm_ex(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k, n,
+                                    fp8q.OUT_BF16, acc, dx.data_ptr(), k, sp)
+        r = clock.stats(fg, reps, flop=flop, nbytes=nbytes)
+        r.update(roofline_entry(flop, nbytes, r["median_us"]))
+        out[f"dgrad_{m}x{k}x{n}{acc_name}"] = r
     return out
 
 
-def _burst_us(torch, stream, fn, reps=20):
-    """Average of `reps` launches started after 200 ms without GPU work.  The
-    HBM-bound kernels run at their full rate for the first ~1.5 ms of
-    sustained load and slower after that (the GPU's power management; the
-    sustained average is the figure the roofline fraction uses)."""
-    torch.cuda.synchronize()
-    time.sleep(0.2)
-    return _event_us(torch, stream, fn, reps)
+# ------------------------------------------------------ CPU baseline ----
+
+def cpu_baseline(step_outputs):
+    """The oracle, as it stands, on the host cores, on bounded samples of
+    each configuration (quantize and GEMM timed apart), and a parity check of
+    a sample of the timed step's outputs against it.
+
+    `value` is the oracle's block-scaled GEMM rate on the dense up-projection
+    sample (the headline metric's GEMM)."""
+    import threadpoolctl
+
+    import synth
+    from oracle import gemm as G, quantize as Q
+
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    with threadpoolctl.threadpool_limits(cores):
+        def timed(f):
+            t0 = time.perf_counter()
+            v = f()
+            return v, time.perf_counter() - t0
+
+        # 1: the whole tiny linear
+        d = synth.tiny_linear()
+        (qa, tqa) = timed(lambda: Q.quantize_rows(d["a"]))
+        (qw, tqw) = timed(lambda: Q.quantize_blocks(d["w"]))
+        (_, tg) = timed(lambda: G.gemm(qa[0], qa[1], qw[0], qw[1]))
+        b1 = d["a"].size * 3.03125 + d["w"].size * 3.0
+        res["1_tiny_linear"] = {"quantize_s": round(tqa + tqw, 4), "quantize_GB/s": round(b1 / (tqa + tqw) / 1e9, 4),
+                                "gemm_s": round(tg, 4), "gemm_TFLOP/s": round(2.0 * 128 * 256 * 512 / tg / 1e12, 6),
+                                "sample": "whole workload (A 128x512, W 256x512, C 128x256)"}
+        # 2: dense up-projection, 1024 rows of A and of W
+        d = synth.dense_up()
+        rows = 1024
+        a, w = np.ascontiguousarray(d["a"][:rows]), np.ascontiguousarray(d["w"][:rows])
+        (qa, tqa) = timed(lambda: Q.quantize_rows(a))
+        (qw, tqw) = timed(lambda: Q.quantize_blocks(w))
+        (_, tg) = timed(lambda: G.gemm(qa[0], qa[1], qw[0], qw[1]))
+        gemm2 = 2.0 * rows * rows * K / tg / 1e12
+        b2 = a.size * 3.03125 + w.size * 3.0
+        res["2_dense_up"] = {"quantize_s": round(tqa + tqw, 3), "quantize_GB/s": round(b2 / (tqa + tqw) / 1e9, 4),
+                             "gemm_s": round(tg, 3), "gemm_TFLOP/s": round(gemm2, 5),
+                             "sample": f"A rows 0..{rows - 1}, W rows 0..{rows - 1}: GEMM {rows}x{rows}x{K}"}
+        # 3: quantize-only, 1024 activation rows per mode and 1024 weight rows
+        act = synth.quant_only_act()[:1024]
+        (_, tf) = timed(lambda: Q.quantize_rows(act, Q.FREE))
+        (_, tp) = timed(lambda: Q.quantize_rows(act, Q.POW2))
+        wt = synth.quant_only_weight()[:1024]
+        (_, tw) = timed(lambda: Q.quantize_blocks(wt))
+        res["3_quantize_only"] = {"act_free_GB/s": round(act.size * 3.03125 / tf / 1e9, 4),
+                                  "act_pow2_GB/s": round(act.size * 3.03125 / tp / 1e9, 4),
+                                  "weight_GB/s": round(wt.size * 3.0 / tw / 1e9, 4),
+                                  "seconds": round(tf + tp + tw, 3),
+                                  "sample": "activation rows 0..1023 (both modes), weight rows 0..1023"}
+        # 4: MoE: the busiest hosted expert's first 512 rows, up-projection
+        md = synth.moe_grouped()
+        e = int(np.argmax(md["counts"]))
+        lo = int(md["offsets"][e])
+        xr = md["x"][md["gather"][lo:lo + 512]]
+        (qx, tq) = timed(lambda: Q.quantize_rows(xr))
+        (qwe, tqw) = timed(lambda: Q.quantize_blocks(md["w_up"][e][:1024]))
+        (_, tg) = timed(lambda: G.gemm(qx[0], qx[1], qwe[0], qwe[1]))
+        res["4_moe_grouped"] = {"quantize_s": round(tq + tqw, 3), "gemm_s": round(tg, 3),
+                                "gemm_TFLOP/s": round(2.0 * xr.shape[0] * 1024 * xr.shape[1] / tg / 1e12, 5),
+                                "sample": f"expert {e}: 512 of its rows x 1024 of its 4096 up-projection columns"}
+        del md
+        # 5: Wgrad: 128 dY features x 512 X features over all 16384 tokens
+        wd = synth.wgrad()
+        (qdy, tq1) = timed(lambda: Q.quantize_token_t(np.ascontiguousarray(wd["dy"][:, :128])))
+        (qx5, tq2) = timed(lambda: Q.quantize_token_t(np.ascontiguousarray(wd["x"][:, :512])))
+        (_, tg) = timed(lambda: G.wgrad(qdy[0], qdy[1], qx5[0], qx5[1]))
+        t_tok = wd["dy"].shape[0]
+        res["5_wgrad"] = {"quantize_s": round(tq1 + tq2, 3),
+                          "quantize_GB/s": round(t_tok * 640 * 3.03125 / (tq1 + tq2) / 1e9, 4),
+                          "gemm_s": round(tg, 3), "gemm_TFLOP/s": round(2.0 * 128 * 512 * t_tok / tg / 1e12, 5),
+                          "sample": f"dW[0:128, 0:512] over {t_tok} tokens"}
+        del wd
+        parity = step_parity(step_outputs, synth, Q, G)
+    total = sum(v.get("seconds", v.get("quantize_s", 0) + v.get("gemm_s", 0)) for v in res.values())
+    blas = [i.get("num_threads") for i in threadpoolctl.threadpool_info()]
+    return {"value": res["2_dense_up"]["gemm_TFLOP/s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "the oracle's block-scaled GEMM on 1024 rows of A and W of the 4096x4096x7168 workload "
+                      f"(value); every configuration's sample timed apart in per_config ({total:.1f} s in all)",
+            "blas_threads": blas, "per_config": res, "parity_on_timed_outputs": parity}
 
 
-def flushed_launch_us(torch, stream, fn, reps=20):
-    """Median and min of single launches, each after a 1 GiB buffer (more
-    than the 256 MB Infinity Cache and every L2) has been written, with one
-    HIP event pair per launch."""
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    times = []
-    for i in range(reps):
-        scratch.fill_(i & 0xFF)
-        e0.record(stream)
-        if fn() != 0:
-            raise RuntimeError("fp8q call failed")
-        e1.record(stream)
-        e1.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3)
-    del scratch
-    return float(np.median(times)), float(np.min(times))
+def step_parity(outs, synth, Q, G):
+    """A sample of the timed step's outputs against the oracle: 16 rows of A
+    and two 128-row weight blocks, codes and scales bit for bit, and the
+    4096 C elements they span within the BF16 tolerance rule."""
+    a_codes, a_scales, w_codes, w_scales, c_bits = outs
+    d = synth.dense_up()
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(M, 16, replace=False))
+    blocks = np.sort(rng.choice(N // 128, 2, replace=False))
+    wrows = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+    qa_c, qa_s = Q.quantize_rows(d["a"][rows])
+    qw_c, qw_s = Q.quantize_blocks(d["w"][wrows])
+    codes_ok = (np.array_equal(a_codes[rows], qa_c) and np.array_equal(a_scales[rows].view(np.uint32),
+                                                                        qa_s.view(np.uint32))
+                and np.array_equal(w_codes[wrows], qw_c)
+                and np.array_equal(w_scales[blocks].view(np.uint32), qw_s.view(np.uint32)))
+    ref, s = G.gemm(qa_c, qa_s, qw_c, qw_s)
+    ok = G.accept_bf16(c_bits[np.ix_(rows, wrows)], ref, s)
+    return {"codes_and_scales_bit_exact": bool(codes_ok), "gemm_within_tolerance": int(ok.sum()),
+            "gemm_checked": int(ok.size),
+            "sample": f"A rows {rows.tolist()}, W blocks {blocks.tolist()} (rows {blocks[0] * 128}..+127, "
+                      f"{blocks[1] * 128}..+127)"}
 
 
 def rocm_smi_clocks():
     """Current clocks reported by rocm-smi (read after the measurements), or
     None where it is not available.  rocm-smi is a Python script: it is run
-    by this interpreter as a child process, not through its `env` shebang,
-    so no process that has loaded a profiler's GPU library replaces itself
-    with another program."""
+    by this interpreter as a child process, not through its `env` shebang."""
     import shutil
     import subprocess
     try:
@@ -414,26 +548,14 @@ def rocm_smi_clocks():
         target = os.path.realpath(smi)
         cmd = [sys.executable, target] if target.endswith(".py") else [smi]
         r = subprocess.run(cmd + ["--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        text = r.stdout[r.stdout.index("{"):]
-        cards = json.loads(text)
+        cards = json.loads(r.stdout[r.stdout.index("{"):])
         card = cards[sorted(cards)[0]]
         return {k.strip(" :"): v for k, v in card.items()}
     except Exception:
         return None
 
 
-def _event_us(torch, stream, fn, reps):
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    fn(0)
-    fn(1)
-    e0.record(stream)
-    for i in range(reps):
-        if fn(i) != 0:
-            raise RuntimeError("fp8q call failed")
-    e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
-
+# --------------------------------------------------------------- main ----
 
 def main():
     args = parse()
@@ -441,7 +563,8 @@ def main():
         copy_calibration(args.steps)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "fp8q runs on one GPU only (no multi-GPU path); --gpus must be 1"}))
+        print(json.dumps({"error": "fp8q runs on one GPU only: it has no multi-GPU path (no sharding, no "
+                                   "collectives); run with --gpus 1"}))
         sys.exit(2)
 
     import torch
@@ -451,60 +574,66 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
-    fp8q.load_library()
+    lib = fp8q.load_library()
     dev = torch.device("cuda:0")
     d = synth.dense_up(m=M, n=N, k=K)
-    a = torch.from_numpy(d["a"].view(np.int16)).view(torch.bfloat16).to(dev)
-    w = torch.from_numpy(d["w"].view(np.int16)).view(torch.bfloat16).to(dev)
+    a = bf16_dev(torch, d["a"])
+    w = bf16_dev(torch, d["w"])
     a_codes = torch.empty((M, K), dtype=torch.uint8, device=dev)
     w_codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     a_scales = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
     w_scales = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
     c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    lib = fp8q.load_library()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    clock = Clock(torch, stream)
 
-    def gemm():
-        return lib.fp8q_gemm_ex(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
-                             M, N, K, fp8q.OUT_BF16, fp8q.ACC_FP32, c.data_ptr(), N, sp)
+    def gemm(i=0):
+        return lib.fp8q_gemm(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(), M, N,
+                             K, fp8q.OUT_BF16, c.data_ptr(), N, sp)
 
-    def q_both():
-        # both quantizers in one launch; outputs identical to fp8q_quantize_act +
-        # fp8q_quantize_weight
+    def q_both(i=0):
         return lib.fp8q_quantize_linear(a.data_ptr(), M, K, K, fp8q.SCALE_FREE, a_codes.data_ptr(), K,
                                         a_scales.data_ptr(), w.data_ptr(), N, K, fp8q.SCALE_FREE,
                                         w_codes.data_ptr(), K, w_scales.data_ptr(), sp)
 
-    def step():
-        st = q_both() | gemm()
+    def step(i=0):
+        st = q_both() or gemm()
         if st != fp8q.OK:
             raise RuntimeError(f"fp8q call failed with status {st}")
+        return st
 
+    clock.warm(step, PREWARM_MS)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, nothing else on the stream
+    # timed region: exactly --steps steps; events on the launch stream
+    # bracket each GEMM launch (the GEMM's live duration)
+    g0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    g1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        if q_both() != fp8q.OK:
+            raise RuntimeError("fp8q_quantize_linear failed")
+        g0[i].record(stream)
+        if gemm() != fp8q.OK:
+            raise RuntimeError("fp8q_gemm failed")
+        g1[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     ms_step_events = ev0.elapsed_time(ev1) / args.steps
+    gemm_live_us = float(np.mean([g0[i].elapsed_time(g1[i]) * 1e3 for i in range(args.steps)]))
+    step_outputs = (a_codes.cpu().numpy(), a_scales.cpu().numpy(), w_codes.cpu().numpy(), w_scales.cpu().numpy(),
+                    c.view(torch.int16).cpu().numpy().view(np.uint16))
 
-    # per-kernel durations: HIP events on the launch stream around --steps
-    # back-to-back launches of one kernel (an event record is a queue barrier
-    # packet, so one pair per run keeps it out of the average).  The
-    # quantizers rotate over ROT copies of their input and output (more than
-    # the 256 MB Infinity Cache), so each launch streams from HBM as in the
-    # step; the GEMM re-reads its 58 MB of codes, which in the step were just
-    # written by the quantizers.
-    ROT = 5
+    reps = max(20, args.steps // 2)
+    ROT = 5  # quantizer inputs rotate over 5 copies: more than the Infinity Cache
     a_rot = [a] + [a.clone() for _ in range(ROT - 1)]
     w_rot = [w] + [w.clone() for _ in range(ROT - 1)]
     ac_rot = [torch.empty_like(a_codes) for _ in range(ROT)]
@@ -515,68 +644,74 @@ def main():
                                      ac_rot[i % ROT].data_ptr(), K, a_scales.data_ptr(), sp)
 
     def q_wgt_i(i):
-        return lib.fp8q_quantize_weight(w_rot[i % ROT].data_ptr(), N, K, K, fp8q.SCALE_FREE,
-                                        wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
-
-    def kernel_us(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(ROT):
-            fn(i)
-        e0.record(stream)
-        for i in range(args.steps):
-            fn(i)
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / args.steps
-
-    qa_us = kernel_us(q_act_i)
-    qw_us = kernel_us(q_wgt_i)
+        return lib.fp8q_quantize_weight(w_rot[i % ROT].data_ptr(), N, K, K, fp8q.SCALE_FREE, wc_rot[i % ROT].data_ptr(),
+                                        K, w_scales.data_ptr(), sp)
 
     def q_lin_i(i):
-        return lib.fp8q_quantize_linear(a_rot[i % ROT].data_ptr(), M, K, K, fp8q.SCALE_FREE,
-                                        ac_rot[i % ROT].data_ptr(), K, a_scales.data_ptr(), w_rot[i % ROT].data_ptr(),
-                                        N, K, fp8q.SCALE_FREE, wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
-    ql_us = kernel_us(q_lin_i)
-    gemm_us = kernel_us(lambda i: gemm())
-    gemm_f8_us = kernel_us(lambda i: lib.fp8q_gemm_ex(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
-                                                   w_scales.data_ptr(), M, N, K, fp8q.OUT_BF16,
-                                                   fp8q.ACC_FP8_MFMA, c.data_ptr(), N, sp))
-    # the hardware-scaled form needs power-of-two scales: the same inputs
-    # quantized in that mode
-    ap_codes, ap_scales = fp8q.quantize_act(a, scale_mode="pow2")
-    wp_codes, wp_scales = fp8q.quantize_weight(w, scale_mode="pow2")
-    gemm_f8s_us = kernel_us(lambda i: lib.fp8q_gemm_ex(ap_codes.data_ptr(), ap_scales.data_ptr(),
-                                                    wp_codes.data_ptr(), wp_scales.data_ptr(), M, N, K,
-                                                    fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA_SCALED, c.data_ptr(), N, sp))
-    del ap_codes, ap_scales, wp_codes, wp_scales
-    # the GEMM with its output quantized in the epilogue (1x128 along N, the
-    # FP8 input of a following layer) next to the unfused pair it replaces
+        return lib.fp8q_quantize_linear(a_rot[i % ROT].data_ptr(), M, K, K, fp8q.SCALE_FREE, ac_rot[i % ROT].data_ptr(),
+                                        K, a_scales.data_ptr(), w_rot[i % ROT].data_ptr(), N, K, fp8q.SCALE_FREE,
+                                        wc_rot[i % ROT].data_ptr(), K, w_scales.data_ptr(), sp)
+
+    dense = {"quantize_act_1x128": clock.stats(q_act_i, reps, nbytes=ACT_BYTES),
+             "quantize_weight_128x128": clock.stats(q_wgt_i, reps, nbytes=WGT_BYTES),
+             "quantize_linear_act_and_weight": clock.stats(q_lin_i, reps, nbytes=ACT_BYTES + WGT_BYTES)}
+    dense["quantize_linear_after_cache_flush"] = clock.stats(lambda i: q_lin_i(0), 20, nbytes=ACT_BYTES + WGT_BYTES,
+                                                             flush=True)
+    del a_rot, w_rot, ac_rot, wc_rot
+    q_both()  # the step's codes again, for the GEMMs below
+
+    # GEMM forms; the quantized-output GEMM next to the GEMM + quantizer pair
+    # it replaces, measured in alternating rounds so all three see one clock
     cq = torch.empty((M, N), dtype=torch.uint8, device=dev)
     cqs = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
-    gemm_q_us = kernel_us(lambda i: lib.fp8q_gemm_quantized(a_codes.data_ptr(), a_scales.data_ptr(),
-                                                            w_codes.data_ptr(), w_scales.data_ptr(), M, N, K,
-                                                            fp8q.ACC_FP32, fp8q.SCALE_FREE, cq.data_ptr(), N,
-                                                            cqs.data_ptr(), sp))
+
+    def fused(i):
+        return lib.fp8q_gemm_quantized(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(),
+                                       w_scales.data_ptr(), M, N, K, fp8q.ACC_FP32, fp8q.SCALE_FREE, cq.data_ptr(), N,
+                                       cqs.data_ptr(), sp)
 
     def unfused(i):
-        st = gemm()
-        return st or lib.fp8q_quantize_act(c.data_ptr(), M, N, N, fp8q.TILE_ROW, fp8q.SCALE_FREE, cq.data_ptr(),
-                                           N, cqs.data_ptr(), sp)
-    unfused_us = kernel_us(unfused)
+        return gemm() or lib.fp8q_quantize_act(c.data_ptr(), M, N, N, fp8q.TILE_ROW, fp8q.SCALE_FREE, cq.data_ptr(),
+                                               N, cqs.data_ptr(), sp)
+    rounds = {"gemm": [], "fused": [], "unfused": []}
+    for _ in range(3):
+        for name, fn in (("gemm", gemm), ("fused", fused), ("unfused", unfused)):
+            clock.warm(fn, WARM_MS / 2)
+            rounds[name] += clock.launches(fn, max(10, reps // 3))
+    med = {k: float(np.median(v)) for k, v in rounds.items()}
+    dense["gemm_block_scaled"] = {"median_us": round(med["gemm"], 2), "min_us": round(float(np.min(rounds["gemm"])), 2),
+                                  "launches": len(rounds["gemm"]), "TFLOP/s": round(GEMM_FLOP / med["gemm"] / 1e6, 1),
+                                  "frac_fp8_peak": round(GEMM_FLOP / med["gemm"] / 1e6 / FP8_PEAK_TFLOPS, 4),
+                                  "frac_bf16_peak": round(GEMM_FLOP / med["gemm"] / 1e6 / BF16_PEAK_TFLOPS, 4)}
+    dense["gemm_quantized_output"] = {
+        "workload": "the 4096x4096x7168 GEMM whose BF16 result is quantized 1x128 along N in its epilogue, next to "
+                    "the GEMM (BF16 out) followed by the 1x128 quantizer",
+        "fused_median_us": round(med["fused"], 2), "unfused_pair_median_us": round(med["unfused"], 2),
+        "gemm_alone_median_us": round(med["gemm"], 2),
+        "ordered_gemm_le_fused_le_unfused": bool(med["gemm"] <= med["fused"] <= med["unfused"]),
+        "hbm_bytes_saved_per_call": M * N * 2 * 2}
+    flushed = clock.stats(gemm, 20, flop=GEMM_FLOP, flush=True)
+    dense["gemm_block_scaled_after_cache_flush"] = flushed
     del cq, cqs
-    flush_med_us, flush_min_us = flushed_launch_us(torch, stream, gemm)
-    qflush_med_us, qflush_min_us = flushed_launch_us(torch, stream, lambda: q_lin_i(0))
-    quant_only = quantize_only_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
-    dg = dgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4), w)
-    del a_rot, w_rot, ac_rot, wc_rot
-    moe = moe_rates(torch, fp8q, lib, stream, max(3, args.steps // 2))
-    wg = wgrad_rates(torch, fp8q, lib, stream, max(3, args.steps // 4))
-    qa_gbs = ACT_BYTES / (qa_us * 1e-6) / 1e9
-    qw_gbs = WGT_BYTES / (qw_us * 1e-6) / 1e9
-    gemm_tflops = GEMM_FLOP / (gemm_us * 1e-6) / 1e12
-    gemm_f8_tflops = GEMM_FLOP / (gemm_f8_us * 1e-6) / 1e12
-    value = GEMM_FLOP / (ms_step * 1e-3) / 1e12
+    dense["gemm_block_scaled_fp8_mfma"] = clock.stats(
+        lambda i: lib.fp8q_gemm_ex(a_codes.data_ptr(), a_scales.data_ptr(), w_codes.data_ptr(), w_scales.data_ptr(),
+                                   M, N, K, fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA, c.data_ptr(), N, sp), reps, flop=GEMM_FLOP)
+    ap_c, ap_s, wp_c, wp_s = fp8q.quantize_linear(a, w, act_scale_mode="pow2", weight_scale_mode="pow2")
+    dense["gemm_block_scaled_fp8_mfma_scaled_pow2"] = clock.stats(
+        lambda i: lib.fp8q_gemm_ex(ap_c.data_ptr(), ap_s.data_ptr(), wp_c.data_ptr(), wp_s.data_ptr(), M, N, K,
+                                   fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA_SCALED, c.data_ptr(), N, sp), reps, flop=GEMM_FLOP)
+    del ap_c, ap_s, wp_c, wp_s
+    clock.release()
 
+    configs = {"1_tiny_linear": tiny_linear(torch, fp8q, lib, clock, sp), "2_dense_up": dense}
+    configs["dgrad_of_2"] = dgrad(torch, fp8q, lib, clock, sp, reps, w)
+    configs["3_quantize_only"] = quantize_only(torch, fp8q, lib, clock, sp, reps)
+    configs["4_moe_grouped"] = moe(torch, fp8q, lib, clock, sp, reps)
+    configs["5_wgrad"] = wgrad(torch, fp8q, lib, clock, sp, reps)
+
+    traffic = GEMM_TRAFFIC["bytes"] if GEMM_TRAFFIC["source_sha256"] == source_sha256("gemm.hip") else None
+    achieved = GEMM_FLOP / gemm_live_us / 1e6
+    value = GEMM_FLOP / (ms_step * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -585,64 +720,40 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        # the same timed region seen by HIP events on the stream (excludes the
-        # host's launch latency at its start and the wake-up at its end)
-        "ms_per_step_stream_events": round(ms_step_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate, bf16 in/out",
+        "dtype": "e4m3 x e4m3 -> f32 (bf16 in/out)",
         "data": "synthetic (seeded): A ~N(0,1) with 0.1% entries x100, W ~N(0,0.02), BF16",
-        "config": {"workload": "dense expert up-projection: quantize A 4096x7168 (1x128) + W 4096x7168 "
-                               "(128x128) to E4M3 in one launch, block-scaled GEMM 4096x4096x7168 -> BF16",
+        "config": {"workload": "dense expert up-projection: quantize A 4096x7168 (1x128) + W 4096x7168 (128x128) "
+                               "to E4M3 in one launch, block-scaled GEMM 4096x4096x7168 -> BF16",
                    "M": M, "N": N, "K": K, "scale_mode": "free"},
-        "kernels": {
-            "quantize_act_1x128": {"us": round(qa_us, 2), "GB/s": round(qa_gbs, 1),
-                                   "frac_hbm": round(qa_gbs / HBM_PEAK_GBS, 4), "bytes": ACT_BYTES},
-            "quantize_weight_128x128": {"us": round(qw_us, 2), "GB/s": round(qw_gbs, 1),
-                                        "frac_hbm": round(qw_gbs / HBM_PEAK_GBS, 4), "bytes": WGT_BYTES},
-            # both quantizers of the step in one launch (fp8q_quantize_linear)
-            "quantize_linear_act_and_weight": {
-                "us": round(ql_us, 2), "GB/s": round((ACT_BYTES + WGT_BYTES) / ql_us / 1e3, 1),
-                "frac_hbm": round((ACT_BYTES + WGT_BYTES) / ql_us / 1e3 / HBM_PEAK_GBS, 4),
-                "bytes": ACT_BYTES + WGT_BYTES},
-            "gemm_block_scaled": {"us": round(gemm_us, 2), "TFLOP/s": round(gemm_tflops, 1),
-                                  "frac_fp8_mfma": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
-            # the same GEMM with its 128-element partials formed inside the
-            # FP8 matrix core (acc=FP8Q_ACC_FP8_MFMA); not used by the step
-            "gemm_block_scaled_fp8_mfma": {"us": round(gemm_f8_us, 2), "TFLOP/s": round(gemm_f8_tflops, 1),
-                                           "frac_fp8_mfma": round(gemm_f8_tflops / FP8_PEAK_TFLOPS, 4),
-                                           "flop": GEMM_FLOP},
-            # power-of-two scales applied by the matrix core, no promotion
-            # (acc=FP8Q_ACC_FP8_MFMA_SCALED, inputs quantized with pow2 scales)
-            "gemm_block_scaled_fp8_mfma_scaled_pow2": {
-                "us": round(gemm_f8s_us, 2), "TFLOP/s": round(GEMM_FLOP / gemm_f8s_us / 1e6, 1),
-                "frac_fp8_mfma": round(GEMM_FLOP / gemm_f8s_us / 1e6 / FP8_PEAK_TFLOPS, 4), "flop": GEMM_FLOP},
-        },
-        # single launches after a cache flush (the operands come from HBM)
-        "gemm_block_scaled_after_cache_flush": {"median_us": round(flush_med_us, 2), "min_us": round(flush_min_us, 2),
-                                                "launches": 20, "flush": "1 GiB written before each launch"},
-        "quantize_linear_after_cache_flush": {
-            "median_us": round(qflush_med_us, 2), "min_us": round(qflush_min_us, 2),
-            "frac_hbm_median": round((ACT_BYTES + WGT_BYTES) / qflush_med_us / 1e3 / HBM_PEAK_GBS, 4),
-            "launches": 20, "flush": "1 GiB written before each launch"},
-        "gemm_quantized_output": {
-            "workload": "4096x4096x7168 GEMM whose BF16 result is quantized 1x128 along N in the epilogue",
-            "fused_us": round(gemm_q_us, 2), "fused_TFLOP/s": round(GEMM_FLOP / gemm_q_us / 1e6, 1),
-            "unfused_gemm_bf16_plus_quantize_us": round(unfused_us, 2),
-            "hbm_bytes_saved_per_call": M * N * 2 * 2},
-        "quantize_only": quant_only,
-        "moe_grouped": moe,
-        "wgrad": wg,
-        "dgrad": dg,
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": GEMM_TRAFFIC_BYTES},
+        "ms_per_step_stream_events": round(ms_step_events, 4),
+        "prewarm_ms": PREWARM_MS,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "gemm_bs_kernel, dense, float32-grade partials (fp8q_gemm)",
+                     "flop_per_launch": GEMM_FLOP, "algorithmic_bytes_per_launch": GEMM_MIN_BYTES,
+                     "launch_us_in_timed_steps": round(gemm_live_us, 2),
+                     "frac_bf16_matrix_core_peak": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "back_to_back_median_us": dense["gemm_block_scaled"]["median_us"],
+                     "frac_back_to_back": dense["gemm_block_scaled"]["frac_fp8_peak"],
+                     "after_cache_flush_median_us": flushed["median_us"],
+                     "frac_after_cache_flush": flushed["frac_fp8_peak"],
+                     "traffic_source": (GEMM_TRAFFIC["profile"] if traffic is not None else
+                                        "null: the kernel source changed since the counters were taken")},
         "cpu_baseline": None,
+        "configs": configs,
+        "pages_context": {
+            "accumulation_interval_elements": 128,
+            "accumulation_interval_hardware": "H800 tensor cores, four WGMMAs (jp-study.kr doc 258368, 3rd paragraph)",
+            "full_training_h800_gpu_hours": 2.788e6,
+            "full_training_source": "why-be.co.kr wr_id=77087, 1st paragraph",
+            "note": "context only: the pages report no kernel throughput for this path"},
     }
     out["rocm_smi_clocks_after_run"] = rocm_smi_clocks()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(step_outputs)
     print(json.dumps(out), flush=True)
 
 

@@ -5,7 +5,8 @@ host implementation of what the GPU path computes: the E4M3 codec, the online
 max-abs quantizers (1x128 activation tiles, 128x128 weight blocks, 128x1
 token-axis tiles, free or power-of-two scales), the block-scaled GEMM in its
 dense, grouped and weight-gradient forms, the output acceptance rule, the
-accumulation emulators used for the promotion-interval report, and the MoE
+accumulation emulators used for the promotion-interval report (written from
+the pages' description of limited-width accumulation), and the MoE
 glue on either side of the expert GEMMs (FP8 dispatch gather, SwiGLU with
 its 1x128 quantization).
 

@@ -38,7 +38,9 @@ tiny-linear shape, constant-operand closed form, selector weights, zero
 scales, grouped == per-group dense, Wgrad == dense when scales are constant
 per block, the BF16 interval rule on hand-made cases, the quantized-output
 rule accepting the quantization of the exact result and rejecting planted
-code and scale errors).
+code and scale errors, accepting any quantization inside a wide zero-result
+band, and its attained-scale test against all 32,640 enumerated BF16
+scales).
 """
 
 import numpy as np
@@ -196,17 +198,48 @@ def accept_bf16(c_gpu_bf16_bits, c_ref, s_ref):
     return (v >= lo) & (v <= hi)
 
 
+def _scale_attained(s, mode):
+    """True where the float32 scale s (>= 0) is the tile scale of some BF16
+    value v >= 0, i.e. lies in the image of v -> scale(v).
+
+    Power-of-two scales: s is 0 or a power of two between the scales of the
+    smallest and the largest positive BF16 values.  Free scales
+    s = RN32(v / 448): v then lies within 448 * ulp(s) / 2 of 448 * s, an
+    interval that holds at most one BF16 value, one of the BF16 neighbours
+    of 448 * s; those are tried.
+    """
+    from .quantize import FREE, _tile_scale
+
+    s = np.asarray(s, dtype=np.float32)
+    if mode != FREE:
+        ends = _tile_scale((np.array([1, 0x7F7F], dtype=np.uint32) << 16).view(np.float32), mode)
+        m, _ = np.frexp(s.astype(np.float64))
+        return (s == 0) | ((m == 0.5) & (s >= ends[0]) & (s <= ends[1]))
+    with np.errstate(over="ignore"):  # 448 * s beyond float32: no BF16 value reaches it
+        v = (s.astype(np.float64) * 448.0).astype(np.float32)
+    b = (np.ascontiguousarray(v).view(np.uint32) >> 16).astype(np.int64)
+    hit = s == 0
+    for d in (-1, 0, 1):
+        cand = (np.clip(b + d, 0, 0x7F7F).astype(np.uint32) << 16).view(np.float32)
+        hit |= _tile_scale(cand, mode) == s
+    return hit
+
+
 def accept_quantized(codes_gpu, scales_gpu, c_ref, s_ref, mode):
     """Quantized-output rule, per 1x128 tile along N (boolean [M, nb]): the
     GPU tile must be the 1x128 quantization (oracle.quantize) of some BF16
     tensor that passes ``accept_bf16`` elementwise.
 
     Each element's admissible BF16 values form an interval [lo, hi]
-    (``accept_bf16``).  The tile's max-abs then lies between the largest of
-    the smallest admissible magnitudes and the largest of the largest ones;
-    the scale must be the scale of one BF16 value in that range, and each
-    code must lie between the codes of its interval's ends under that scale
-    (the quotient and the E4M3 rounding are monotone in the value).
+    (``accept_bf16``), so its admissible magnitudes run from min_mag (0 when
+    the interval holds 0) to max_mag.  The tile max-abs of an admissible
+    tensor can be any BF16 value between a_lo = max(min_mag) and
+    a_hi = max(max_mag) (set the element with the largest max_mag to it and
+    every other element to its min_mag).  The scale is a non-decreasing
+    function of the max-abs, so the scales of those tensors are exactly the
+    attained scales between scale(a_lo) and scale(a_hi); each code must then
+    lie between the codes of its interval's ends under the GPU's scale (the
+    quotient and the E4M3 rounding are monotone in the value).
     """
     from .e4m3 import decode, encode
     from .quantize import TILE, _tile_scale
@@ -227,17 +260,7 @@ def accept_quantized(codes_gpu, scales_gpu, c_ref, s_ref, mode):
         a_lo = np.max(min_mag[:, sl], axis=1).astype(np.float32)
         a_hi = np.max(max_mag[:, sl], axis=1).astype(np.float32)
         s = scales_gpu[:, b]
-        # the BF16 values between a_lo and a_hi (both BF16 values >= 0) are
-        # consecutive bit patterns
-        b_lo = (a_lo.view(np.uint32) >> 16).astype(np.int64)
-        b_hi = (a_hi.view(np.uint32) >> 16).astype(np.int64)
-        span = b_hi - b_lo
-        s_ok = np.zeros(m, dtype=bool)
-        for k in range(int(min(span.max(initial=0), 64)) + 1):
-            bits = np.minimum(b_lo + k, b_hi).astype(np.uint32) << 16
-            s_ok |= _tile_scale(bits.view(np.float32), mode) == s
-        wide = span > 64  # degenerate tiles: the scale only has to be in range
-        s_ok |= wide & (s >= _tile_scale(a_lo, mode)) & (s <= _tile_scale(a_hi, mode))
+        s_ok = (s >= _tile_scale(a_lo, mode)) & (s <= _tile_scale(a_hi, mode)) & _scale_attained(s, mode)
 
         def codes_of(v):
             vf = v.astype(np.float32)

@@ -19,16 +19,20 @@ Readings taken where the pages are silent:
   gate then up).
 * The quantized value is the BF16 rounding (nearest, ties to even) of the
   exact SwiGLU value: the tensor an unfused SwiGLU would store in BF16 for
-  the quantizer to read.  The GPU forms the value in float32 with an exp of
-  a few ulp, so where the exact value lies within 2^-19 (relative) of the
-  midpoint between two BF16 numbers either neighbour is accepted
-  (``swiglu_accept``); everything else is compared bit for bit.
+  the quantizer to read.  The GPU forms the value in float32 (hardware exp2
+  and reciprocal, one ulp each), whose relative error is below
+  ``swiglu_rel_error_bound()`` (about 2^-20.7); where the exact value lies
+  within BAND_REL = 2^-19 (relative) of the midpoint between two BF16 numbers
+  either neighbour is accepted (``swiglu_accept``); everything else is
+  compared bit for bit.
 * A gather index outside the source rows gives a zero row and a zero scale.
 
 Pins: tests/test_oracle_moe.py (hand-worked gather, gather commutes with the
 1x128 quantizer, closed forms of silu, BF16 rounding against the float32
 path and hand-worked ties, SwiGLU with u = 1 and a large gate reducing to
-the plain quantizer, the acceptance rule rejecting a planted error).
+the plain quantizer, the acceptance rule rejecting a planted error, the
+error bound composed above against a float32 emulation of the kernel's
+arithmetic with its transcendental steps pushed one ulp either way).
 """
 
 import numpy as np
@@ -38,6 +42,35 @@ from .quantize import FREE, TILE, _tile_scale, quantize_rows
 
 BAND_REL = 2.0 ** -19   # ambiguity band around a BF16 rounding midpoint
 BAND_ABS = 2.0 ** -140  # float32 subnormal results carry absolute errors
+
+
+def swiglu_rel_error_bound(exp2_ulp=1.0, rcp_ulp=1.0):
+    """First-order bound on |y32 - y| / |y| for the float32 SwiGLU the GPU
+    forms, composed from the error of each step (u = 2^-24,
+    the float32 unit roundoff):
+
+    * exponent reduction x log2(e) = n + f with log2(e) carried as
+      RN32(log2 e) + RN32(remainder) and two fused multiply-adds: |df| <= 2u
+      (two roundings of a result below 1/2 in magnitude; the 48-bit
+      log2(e) and |x| <= 104 add below 2^-41), so 2^f is off by a factor
+      2^df, relative ln(2) * 2u;
+    * the hardware exp2 on f: exp2_ulp ulp, relative 2u * exp2_ulp; the exact
+      ldexp adds nothing (subnormal t is covered by BAND_ABS):
+      e_t = ln(2) * 2u + 2u * exp2_ulp;
+    * 1 + t rounds (u) and carries t's error scaled by t / (1 + t) <= 1/2;
+      the hardware reciprocal: rcp_ulp ulp (2u * rcp_ulp):
+      e_r = u + e_t / 2 + 2u * rcp_ulp;
+    * sigma = t * r for g < 0 (the larger case): e_t + e_r + u;
+    * g * sigma and (g * sigma) * up: two more roundings, 2u.
+
+    The band BAND_REL must contain this bound; the margin covers the
+    hardware transcendentals' documented one-ulp accuracy being exceeded by
+    up to a factor of about three.
+    """
+    u = 2.0 ** -24
+    e_t = np.log(2.0) * 2 * u + 2 * u * exp2_ulp
+    e_r = u + e_t / 2 + 2 * u * rcp_ulp
+    return e_t + e_r + u + 2 * u
 
 
 def gather_rows(codes, scales, index):

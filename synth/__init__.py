@@ -139,3 +139,30 @@ def swiglu_input(seed=SEED, rows=None, inter=2048):
         rows = int(moe_routing(seed)[1].sum())
     r = streams(seed + 1, 1)
     return bf16_rne(normal(r[0], (rows, 2 * inter), 1.7))
+
+
+def reachable_band(ebits, seed):
+    """Every (x, amax) pair with amax in one BF16 binade and |x| <= amax, as
+    BF16 bit patterns [tiles, 128].
+
+    Row i is a 128-element tile whose element 0 is the amax (random sign) and
+    whose other elements are x values (random signs).  For each of the 128
+    amax significands of binade `ebits` (BF16 exponent field), every BF16
+    magnitude from 0 up to amax appears once.  A tile's scale and codes
+    depend only on (x, amax) pairs, so the tiles of all 255 binades cover
+    every input the 1x128 quantizer can see.
+    """
+    rng = np.random.default_rng(seed)
+    tiles = []
+    for mant in range(128):
+        ab = (ebits << 7) | mant
+        if ab == 0:
+            continue
+        xs = np.arange(0, ab + 1, dtype=np.uint32).astype(np.uint16)
+        xs |= (rng.integers(0, 2, xs.size) << 15).astype(np.uint16)
+        pad = (-xs.size) % 127
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 127)
+        head = np.full((xs.shape[0], 1), ab, np.uint16) | (rng.integers(0, 2, (xs.shape[0], 1)) << 15).astype(np.uint16)
+        tiles.append(np.concatenate([head, xs], axis=1))
+    return np.concatenate(tiles)
+

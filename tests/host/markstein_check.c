@@ -1,0 +1,61 @@
+/* Exhaustive host check of the quantizers' element quotient.
+ *
+ * The 1x128 / 128x128 quantizers form a tile's scale s = RN32(amax / 448)
+ * with an IEEE division, and each element's quotient RN32(x / s) -- the
+ * value the E4M3 rounding then reads -- with one Markstein correction of the
+ * product by the rounded reciprocal (M. Markstein, "Computation of
+ * elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
+ * Dev. 34(1), 1990):
+ *   r = RN32(1 / s), q0 = RN32(x * r), e = fma(-q0, s, x), q = fma(e, r, q0).
+ * For every BF16 amax >= 2^-90 (exponent field >= 37; smaller tiles divide
+ * per element) and every BF16 x with |x| <= amax this program checks that q
+ * equals the IEEE quotient x / s, or that both are at most 2^-10 in
+ * magnitude (then both encode to the E4M3 zero of x's sign).  Each step is
+ * odd in x, so x >= 0 covers the negatives.
+ *
+ * Build: gcc -O2 -mfma -ffp-contract=off markstein_check.c -o markstein_check
+ * (fmaf must be a single rounding: the hardware instruction with -mfma, or
+ * glibc's correctly rounded fmaf).  Prints the counts and returns 0 when
+ * every pair agrees.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+static float bf16(uint32_t bits) {
+  uint32_t u = bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+int main(void) {
+  const float tiny = 0x1p-10f;
+  uint64_t pairs = 0, equal = 0, both_zero = 0, bad = 0;
+  for (uint32_t ab = 37u << 7; ab <= 0x7F7Fu; ++ab) {
+    const float amax = bf16(ab);
+    const float s = amax / 448.0f;
+    const float r = 1.0f / s;
+    for (uint32_t xb = 0; xb <= ab; ++xb) {
+      const float x = bf16(xb);
+      const float ieee = x / s;
+      const float q0 = x * r;
+      const float e = fmaf(-q0, s, x);
+      const float q = fmaf(e, r, q0);
+      ++pairs;
+      if (q == ieee) {
+        ++equal;
+      } else if (fabsf(q) <= tiny && fabsf(ieee) <= tiny) {
+        ++both_zero;
+      } else {
+        if (bad < 10)
+          printf("mismatch: amax bits 0x%04x x bits 0x%04x: markstein %a ieee %a\n", ab, xb, q, ieee);
+        ++bad;
+      }
+    }
+  }
+  printf("pairs %llu equal %llu both-below-2^-10 %llu mismatches %llu\n", (unsigned long long)pairs,
+         (unsigned long long)equal, (unsigned long long)both_zero, (unsigned long long)bad);
+  return bad == 0 ? 0 : 1;
+}

@@ -21,7 +21,8 @@ import torch
 
 import fine_grained_fp8_fp8q_amd as fp8q
 import synth
-from oracle import accum, gemm as G, quantize as Q
+from oracle import gemm as G, quantize as Q
+from tests import fp8_unit_model as unit
 from tests.gpu_util import (assert_codes_equal, assert_scales_equal, dev, dev_bf16, host, host_bf16_bits,
                             host_codes, need_gpu, say)
 
@@ -105,7 +106,7 @@ def test_dgrad_up_projection_sampled():
             if acc == "fp32":
                 ref, s = G.gemm_at(dy_c, dy_s, wt_c, wt_s, r, q)
             else:
-                ref, s, t = accum.gemm_at_mfma(dy_c, dy_s, wt_c, wt_s, r, q)
+                ref, s, t = unit.gemm_at_mfma(dy_c, dy_s, wt_c, wt_s, r, q)
                 s = s + (2.0 ** -19) * t / 1e-5
             ok = G.accept_bf16(dx[r, q], ref, s)
             assert ok.all(), f"dgrad {acc} chunk {lo}: {int((~ok).sum())} bad"

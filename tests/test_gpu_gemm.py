@@ -19,6 +19,7 @@ import torch
 
 import fine_grained_fp8_fp8q_amd as fp8q
 from oracle import e4m3, gemm as G, quantize as Q
+from tests import fp8_unit_model as unit
 import synth
 from tests.gpu_util import dev, host, host_bf16_bits, moe_operands, need_gpu, say
 
@@ -142,6 +143,15 @@ def test_dense_up_projection_sampled():
         ref, s = G.gemm_at(a_c, a_s, w_c, w_s, r, q)
         ok = G.accept_bf16(cb[r, q], ref, s)
         assert ok.all(), f"dense sampled chunk {lo}: {int((~ok).sum())} bad"
+    # every element of whole 256 x 256 output tiles (one workgroup each): the
+    # corners and one tile of each XCD's tile range (XCD x runs tile rows
+    # 4(x//2)..+3 and tile columns 8(x%2)..+7 of the 16 x 16 tile grid)
+    tiles = [(0, 0), (15, 15), (0, 15), (15, 0)] + [(4 * (x // 2) + x % 4, 8 * (x % 2) + x) for x in range(8)]
+    for tm, tn in tiles:
+        r0, c0 = 256 * tm, 256 * tn
+        ref, s = G.gemm(a_c[r0:r0 + 256], a_s[r0:r0 + 256], w_c[c0:c0 + 256], w_s[c0 // 128:c0 // 128 + 2])
+        ok = G.accept_bf16(cb[r0:r0 + 256, c0:c0 + 256], ref, s)
+        assert ok.all(), f"dense tile ({tm}, {tn}): {int((~ok).sum())} of 65536 bad"
 
 
 def _grouped_case(tokens, hidden, inter, with_down):
@@ -193,6 +203,16 @@ def test_grouped_moe_one_gpu_share_sampled():
             ref, s = G.gemm_at(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rows - lo, cols)
             ok = G.accept_bf16(cb[rows, cols], ref, s)
             assert ok.all(), f"grouped {name} expert {gi}: {int((~ok).sum())} bad"
+            # every element of the expert's first output tile and of its last
+            # (ragged in M unless the expert's rows are a multiple of 256;
+            # both N, 4096 and 7168, are multiples of 256)
+            n = wc.shape[1]
+            last_m = lo + ((hi - lo - 1) // 256) * 256
+            for r0, c0 in {(lo, 0), (last_m, n - 256)}:
+                r1 = min(r0 + 256, hi)
+                ref, s = G.gemm(a_c[r0:r1], a_s[r0:r1], wc[gi][c0:c0 + 256], ws[gi][c0 // 128:c0 // 128 + 2])
+                ok = G.accept_bf16(cb[r0:r1, c0:c0 + 256], ref, s)
+                assert ok.all(), f"grouped {name} expert {gi} tile rows {r0}..{r1}: {int((~ok).sum())} bad"
 
 
 def test_grouped_offsets_past_rows_cap_are_clamped():
@@ -274,7 +294,7 @@ def test_wgrad_tile_widths(acc):
     rows = np.concatenate([np.arange(nout), rng.integers(0, nout, kin), rng.integers(0, nout, 3000)])
     cols = np.concatenate([rng.integers(0, kin, nout), np.arange(kin), rng.integers(0, kin, 3000)])
     got = dw[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()]
-    ref, s, tt = accum.gemm_at_mfma(ops[0], ops[1], ops[2], ops[3], rows, cols, w_block_rows=False)
+    ref, s, tt = unit.gemm_at_mfma(ops[0], ops[1], ops[2], ops[3], rows, cols, w_block_rows=False)
     _accept_model(got, ref, s, tt, "wgrad 256-column tiles, FP8 unit")
 
 
@@ -291,6 +311,13 @@ def test_wgrad_full_sampled():
         ref, s = G.gemm_at(ops[0], ops[1], ops[2], ops[3], r, q, w_block_rows=False)
         ok = G.accept_f32(dw[r, q], ref, s)
         assert ok.all(), f"wgrad chunk {lo}: {int((~ok).sum())} bad"
+    # every element of whole output tiles: the launch uses 256 x 224 tiles
+    # here (8 x 32 of them); first, last and four more spread over the grid
+    for tm, tn in [(0, 0), (7, 31), (3, 5), (4, 16), (1, 30), (6, 11)]:
+        r0, c0 = 256 * tm, 224 * tn
+        ref, s = G.wgrad(ops[0][r0:r0 + 256], ops[1][r0:r0 + 256], ops[2][c0:c0 + 224], ops[3][c0:c0 + 224])
+        ok = G.accept_f32(dw[r0:r0 + 256, c0:c0 + 224], ref, s)
+        assert ok.all(), f"wgrad tile ({tm}, {tn}): {int((~ok).sum())} bad"
 
 
 def test_gemm_deterministic():

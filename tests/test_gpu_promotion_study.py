@@ -34,6 +34,7 @@ import synth
 from gpu_util import (assert_codes_equal, assert_scales_equal, dev_bf16, host, host_codes, need_gpu,
                       say)
 from oracle import accum, gemm as G, quantize as Q
+import fp8_unit_model as unit
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +84,7 @@ def test_promotion_study():
               # partials formed inside the FP8 matrix core (limited-width
               # alignment), promoted every 128 as above
               "gpu_fp8_mfma_interval_128": _stats(dw_mfma[rows, cols], exact, s)}
-    model, _, _ = accum.gemm_at_mfma(dyc, dys, xc, xs, ri, ci, w_block_rows=False)
+    model, _, _ = unit.gemm_at_mfma(dyc, dys, xc, xs, ri, ci, w_block_rows=False)
     report["emulated_fp8_mfma_interval_128"] = _stats(model, exact, s)
     say("[study] emulators")
     terms = accum.dequantized_products(dyc[ri], dys[ri], xc[ci], xs[ci])

@@ -1,11 +1,13 @@
 """GPU parity of the quantizers against the oracle: codes and scales must be
 bit-identical (jp-study.kr doc 258368 ¶1; tmdrlife.com wr_id=13334 ¶4).
 
-Covers the tiny-linear and dense-expert inputs in full, the quantize-only
-workload (16384 x 7168 activations in both scale modes, 7168 x 18432 weights)
-on sampled rows and block rows, ragged and strided shapes, special values,
-the exhaustive reachable (x, amax) space of several exponent bands, and
-run-to-run determinism.
+Covers every input of the five workloads in full: the tiny-linear and
+dense-expert inputs, the quantize-only workload (16384 x 7168 activations in
+both scale modes, 7168 x 18432 weights), and the weight-gradient operands
+(16384 x 2048 and 16384 x 7168 in token tiles, both modes); ragged and
+strided shapes, special values, the exhaustive reachable (x, amax) space of
+every exponent band (against oracle digests) and of several bands element by
+element, and run-to-run determinism.
 """
 
 import numpy as np
@@ -132,60 +134,72 @@ def test_special_values(mode):
     assert_scales_equal(host(s), ws, "special blocks")
 
 
-def reachable_band(ebits, seed):
-    """Every (x, amax) pair with amax in one BF16 binade and |x| <= amax.
-
-    Row i of the result is a 128-element tile whose element 0 is the amax
-    (random sign) and whose other elements are x values (random signs).  For
-    each of the 128 amax significands of the binade, all BF16 magnitudes from
-    0 up to amax are covered.
-    """
-    rng = np.random.default_rng(seed)
-    tiles = []
-    for mant in range(128):
-        ab = (ebits << 7) | mant
-        if ab == 0:
-            continue
-        xs = np.arange(0, ab + 1, dtype=np.uint32).astype(np.uint16)
-        xs |= (rng.integers(0, 2, xs.size) << 15).astype(np.uint16)
-        pad = (-xs.size) % 127
-        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 127)
-        head = np.full((xs.shape[0], 1), ab, np.uint16) | (rng.integers(0, 2, (xs.shape[0], 1)) << 15).astype(np.uint16)
-        tiles.append(np.concatenate([head, xs], axis=1))
-    return np.concatenate(tiles)
-
-
 @pytest.mark.parametrize("ebits", [0, 1, 36, 37, 100, 127, 160, 254])
 @pytest.mark.parametrize("mode", ["free", "pow2"])
 def test_exhaustive_reachable_space(ebits, mode):
-    bits = reachable_band(ebits, seed=ebits)
+    bits = synth.reachable_band(ebits, seed=ebits)
     _check_rows(bits, mode, f"reachable band e={ebits}")
 
 
+def _band_digests():
+    from tests.conftest import golden_lines
+    return {(int(e), m): (int(n), h) for e, m, n, h in golden_lines("reachable_band_digests.txt")}
+
+
 @pytest.mark.parametrize("mode", ["free", "pow2"])
-def test_quantize_only_activations_sampled_rows(mode):
+def test_exhaustive_reachable_space_every_band(mode):
+    """All 255 BF16 exponent fields of amax, every x with |x| <= amax (530
+    million (x, amax) pairs per mode): the GPU's codes and scales hash to the
+    digests the oracle's quantization of the same tiles gives
+    (tests/golden/make_band_digests.py).  A mismatching band is then compared
+    element by element with the oracle for the report."""
+    import hashlib
+    want = _band_digests()
+    say(f"[quant] every reachable band, {mode}")
+    bad = []
+    for ebits in range(255):
+        bits = synth.reachable_band(ebits, seed=ebits)
+        n, digest = want[(ebits, mode)]
+        assert bits.shape[0] == n, (ebits, bits.shape, n)
+        codes, scales = fp8q.quantize_act(dev_bf16(bits), tile_axis="row", scale_mode=mode)
+        h = hashlib.sha256()
+        h.update(host_codes(codes).tobytes())
+        h.update(np.ascontiguousarray(host(scales), dtype="<f4").tobytes())
+        if h.hexdigest() != digest:
+            bad.append(ebits)
+            if len(bad) == 1:  # report the first difference of the first bad band
+                wc, ws = Q.quantize_rows(bits, mode)
+                assert_scales_equal(host(scales), ws, f"band e={ebits} scales")
+                assert_codes_equal(host_codes(codes), wc, f"band e={ebits} codes")
+    assert not bad, f"bands with differences: {bad}"
+
+
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_quantize_only_activations_full(mode):
+    """The quantize-only activations 16384 x 7168 (standard Student-t(3)),
+    every code and scale, compared in chunks of 2048 rows."""
     act = synth.quant_only_act()
-    say(f"[quant] quantize-only activations 16384x7168 {mode}")
+    say(f"[quant] quantize-only activations 16384x7168 {mode}, every element")
     codes, scales = fp8q.quantize_act(dev_bf16(act), "row", mode)
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([np.arange(64), np.arange(act.shape[0] - 64, act.shape[0]),
-                                     rng.integers(0, act.shape[0], 192)]))
-    wc, ws = Q.quantize_rows(act[rows], mode)
-    idx = torch.from_numpy(rows).to(codes.device)
-    assert_codes_equal(host_codes(codes.index_select(0, idx)), wc, "act rows")
-    assert_scales_equal(host(scales.index_select(0, idx)), ws, "act rows")
+    sc = host(scales)
+    for r0 in range(0, act.shape[0], 2048):
+        wc, ws = Q.quantize_rows(act[r0:r0 + 2048], mode)
+        assert_codes_equal(host_codes(codes[r0:r0 + 2048]), wc, f"act rows {r0}..")
+        assert_scales_equal(sc[r0:r0 + 2048], ws, f"act rows {r0}..")
 
 
-def test_quantize_only_weights_sampled_block_rows():
+def test_quantize_only_weights_full():
+    """The quantize-only weights 7168 x 18432 (~N(0, 0.02)) per 128 x 128
+    block, every code and scale, compared in chunks of 8 block rows."""
     w = synth.quant_only_weight()
-    say("[quant] quantize-only weights 7168x18432")
+    say("[quant] quantize-only weights 7168x18432, every element")
     codes, scales = fp8q.quantize_weight(dev_bf16(w), "free")
     sc = host(scales)
-    for bi in (0, 27, 55):
-        lo, hi = bi * 128, (bi + 1) * 128
+    for bi in range(0, w.shape[0] // 128, 8):
+        lo, hi = bi * 128, (bi + 8) * 128
         wc, ws = Q.quantize_blocks(w[lo:hi], "free")
-        assert_codes_equal(host_codes(codes[lo:hi]), wc, f"weight block row {bi}")
-        assert_scales_equal(sc[bi:bi + 1], ws, f"weight block row {bi}")
+        assert_codes_equal(host_codes(codes[lo:hi]), wc, f"weight block rows {bi}..{bi + 7}")
+        assert_scales_equal(sc[bi:bi + 8], ws, f"weight block rows {bi}..{bi + 7}")
 
 
 def test_dense_up_projection_inputs_full():
@@ -198,10 +212,23 @@ def test_dense_up_projection_inputs_full():
     assert_scales_equal(host(s), ws, "dense W")
 
 
-def test_wgrad_inputs_token_axis_sampled():
-    d = synth.wgrad(tokens=4096)
-    _check_rows(d["dy"], "free", "wgrad dY 4096x2048", tile_axis="token_t")
-    _check_rows(d["x"][:, :1024], "pow2", "wgrad X 4096x1024", tile_axis="token_t")
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_wgrad_inputs_token_axis_full(mode):
+    """The weight-gradient operands at full size, dY 16384 x 2048 and
+    X 16384 x 7168 in 128-token x 1-feature tiles (codes written
+    feature-major): every code and scale, in chunks of 1024 features."""
+    d = synth.wgrad()
+    for name in ("dy", "x"):
+        bits = d[name]
+        t, f = bits.shape
+        say(f"[quant] wgrad {name} {t}x{f} token tiles {mode}, every element")
+        codes, scales = fp8q.quantize_act(dev_bf16(bits), tile_axis="token_t", scale_mode=mode)
+        sc = host(scales)
+        for c0 in range(0, f, 1024):
+            wc, ws = Q.quantize_token_t(np.ascontiguousarray(bits[:, c0:c0 + 1024]), mode)
+            assert_codes_equal(host_codes(codes[c0:c0 + 1024]), wc, f"{name} features {c0}..")
+            assert_scales_equal(sc[c0:c0 + 1024], ws, f"{name} features {c0}..")
+        del codes, scales
 
 
 def test_quantize_then_gather_equals_gather_then_quantize():

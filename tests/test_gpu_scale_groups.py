@@ -22,7 +22,8 @@ import torch
 
 import fine_grained_fp8_fp8q_amd as fp8q
 import synth
-from oracle import accum, gemm as G, quantize as Q
+from oracle import gemm as G, quantize as Q
+from tests import fp8_unit_model as unit
 from tests.gpu_util import dev, host, need_gpu, say
 from tests.test_gpu_gemm import _accept
 from tests.test_gpu_native import _accept_chained, _accept_model
@@ -77,7 +78,7 @@ def test_dense_scale_groups(nkb, acc):
     rows, cols = _sample(rng, m, n)
     got = c[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()]
     if acc == "fp8_mfma":
-        ref, s, t = accum.gemm_at_mfma(a_c, a_s, w_c, w_s, rows, cols)
+        ref, s, t = unit.gemm_at_mfma(a_c, a_s, w_c, w_s, rows, cols)
         _accept_model(got, ref, s, t, f"dense fp8 unit k/128={nkb}")
     else:
         _accept_chained(host(got).astype(np.float64), a_c, a_s, w_c, w_s, rows, cols,
@@ -110,7 +111,7 @@ def test_grouped_scale_groups(acc, n):
             continue
         rr, cc = _sample(rng, hi - lo, n)
         got = c[torch.from_numpy(rr + lo).cuda(), torch.from_numpy(cc).cuda()]
-        ref, s, t = accum.gemm_at_mfma(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rr, cc)
+        ref, s, t = unit.gemm_at_mfma(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], rr, cc)
         _accept_model(got, ref, s, t, f"grouped fp8 unit N={n} expert {gi}")
 
 
@@ -134,5 +135,5 @@ def test_wgrad_scale_groups(nkb, acc):
         return
     rr, cc = _sample(rng, nout, kin)
     got = dw[torch.from_numpy(rr).cuda(), torch.from_numpy(cc).cuda()]
-    ref, s, t = accum.gemm_at_mfma(dy_c, dy_s, x_c, x_s, rr, cc, w_block_rows=False)
+    ref, s, t = unit.gemm_at_mfma(dy_c, dy_s, x_c, x_s, rr, cc, w_block_rows=False)
     _accept_model(got, ref, s, t, f"wgrad fp8 unit k/128={nkb}")

@@ -234,3 +234,50 @@ def test_block_spread_inputs_expose_misplaced_scales():
     swap_row = a_s.copy(); swap_row[[16, 17], 0] = a_s[[17, 16], 0]     # two rows of one 16-row quarter
     swap_w = w_s.copy(); swap_w[1, [0, 4]] = w_s[1, [4, 0]]              # W block column 1, blocks 0 and 4
     assert fails(swap_block) and fails(swap_group) and fails(swap_row) and fails(a_s, swap_w)
+
+
+@pytest.mark.parametrize("mode", [Q.FREE, Q.POW2])
+def test_scale_attained_against_brute_force(mode):
+    """The scales of all 32,640 non-negative finite BF16 values, enumerated,
+    against the closed-form membership test: every attained scale is
+    recognised, and float32 values next to them (or random ones) are
+    recognised exactly when they are in the enumerated set."""
+    v = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    attained = Q._tile_scale(v, mode)
+    assert G._scale_attained(attained, mode).all()
+    table = set(attained.view(np.uint32).tolist())
+    rng = np.random.default_rng(8)
+    probe = np.concatenate([np.nextafter(attained, np.float32(np.inf)),
+                            np.nextafter(attained, np.float32(0)),
+                            rng.integers(0, 0x7F7FFFFF, 200000).astype(np.uint32).view(np.float32)])
+    want = np.array([b in table for b in probe.view(np.uint32).tolist()])
+    assert np.array_equal(G._scale_attained(probe, mode), want)
+
+
+@pytest.mark.parametrize("mode", [Q.FREE, Q.POW2])
+def test_acceptance_rule_quantized_degenerate_tile(mode):
+    """A tile whose exact results are all zero but whose tolerance is wide
+    (S = 1000: every element may be any BF16 value in [-0.01, 0.01]): the
+    quantization of any BF16 tensor inside that band is accepted, whatever
+    its max-abs; a scale above the band's, or one that no BF16 max-abs
+    yields, is rejected.  (Every code is admissible here: any value up to
+    448 * s lies inside the band.)"""
+    c = np.zeros((3, 128))
+    s = np.full((3, 128), 1000.0)
+    rng = np.random.default_rng(4)
+    rows = []
+    for top in (0.0078125, 2.0 ** -12, 0.009):  # max-abs of each row (BF16 values)
+        x = rng.uniform(-top, top, 128).astype(np.float32)
+        x[17] = top
+        rows.append(e4m3.f32_to_bf16_bits_rne(x))
+    bits = np.stack(rows)
+    codes, scales = Q.quantize_rows(bits, mode)
+    assert G.accept_quantized(codes, scales, c, s, mode).all()
+    high = scales.copy()
+    high[0, 0] = Q._tile_scale(np.float32(0.05), mode)
+    assert not G.accept_quantized(codes, high, c, s, mode)[0, 0]
+    if mode == Q.FREE:
+        odd = scales.copy()
+        odd[1, 0] = np.nextafter(scales[1, 0], np.float32(1))  # not RN32(v/448) of any BF16 v
+        assert not G._scale_attained(odd[1:2, 0], mode)[0]
+        assert not G.accept_quantized(codes, odd, c, s, mode)[1, 0]

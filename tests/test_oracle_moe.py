@@ -123,3 +123,66 @@ def test_candidates_only_near_midpoints():
     # a midpoint between two BF16 numbers and its neighbours on the grid
     lo, hi, q = moe._bf16_grid(np.array([1 + 2.0 ** -8, -(1 + 2.0 ** -8)]))
     assert lo.tolist() == [1.0, -(1 + 2.0 ** -7)] and hi.tolist() == [1 + 2.0 ** -7, -1.0]
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def _ulp_push(x32, k):
+    """float32 values moved k ulps (k = -1, 0, 1) toward +inf / -inf."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    if k > 0:
+        return np.nextafter(x32, np.float32(np.inf))
+    if k < 0:
+        return np.nextafter(x32, np.float32(-np.inf))
+    return x32
+
+
+def _swiglu_f32(g, u, k_exp, k_rcp):
+    """The GPU's float32 SwiGLU sequence, emulated step by step: the two-part
+    log2(e) reduction with fused multiply-adds (exact products in float64,
+    one rounding each), exp2 and the reciprocal correctly rounded and then
+    pushed k ulps (the hardware's one-ulp accuracy), ldexp exact."""
+    g = _f32(g)
+    u = _f32(u)
+    x = np.maximum(-np.abs(g), np.float32(-104.0))
+    hi = np.float32(1.44269502162933349609375)
+    lo = np.float32(1.92596298909109e-8)
+    n = np.rint(_f32(x.astype(np.float64) * hi))
+    f1 = _f32(x.astype(np.float64) * hi - n)
+    f = _f32(x.astype(np.float64) * lo + f1)
+    p = _ulp_push(_f32(np.exp2(f.astype(np.float64))), k_exp)
+    t = _f32(np.ldexp(p.astype(np.float64), n.astype(np.int64)))
+    r = _ulp_push(_f32(1.0 / _f32(1.0 + t.astype(np.float64)).astype(np.float64)), k_rcp)
+    sg = np.where(g >= 0, r, _f32(t.astype(np.float64) * r))
+    return _f32(_f32(g.astype(np.float64) * sg).astype(np.float64) * u)
+
+
+def test_swiglu_error_bound_holds_and_sits_inside_the_band():
+    """The composed bound (oracle.moe.swiglu_rel_error_bound) against an
+    emulation of the kernel's float32 arithmetic on 200,000 BF16 (gate, up)
+    pairs spread over gates in [-40, 40] (and tails to -104), with the
+    hardware exp2 and reciprocal results pushed one ulp up or down: every
+    emulated result is within the bound of the exact value, and the bound is
+    inside the acceptance band BAND_REL."""
+    bound = moe.swiglu_rel_error_bound()
+    assert bound < moe.BAND_REL / 2
+    rng = np.random.default_rng(11)
+    g = np.concatenate([rng.uniform(-40, 40, 150000), rng.uniform(-104, -40, 25000),
+                        rng.standard_normal(25000) * 1.7]).astype(np.float32)
+    ub = rng.standard_normal(g.size).astype(np.float32)
+    gb = e4m3.bf16_bits_to_f32(_bits(g)).astype(np.float64)
+    uv = e4m3.bf16_bits_to_f32(_bits(ub)).astype(np.float64)
+    exact = moe.silu(gb) * uv
+    worst = 0.0
+    for k_exp in (-1, 0, 1):
+        for k_rcp in (-1, 0, 1):
+            y = _swiglu_f32(gb, uv, k_exp, k_rcp).astype(np.float64)
+            err = np.abs(y - exact)
+            ok = err <= bound * np.abs(exact) + moe.BAND_ABS
+            assert ok.all(), (k_exp, k_rcp, gb[~ok][:3], (err / np.abs(exact))[~ok][:3])
+            normal = np.abs(exact) > 2.0 ** -100
+            worst = max(worst, float((err[normal] / np.abs(exact[normal])).max()))
+    # the bound is not loose by orders of magnitude either
+    assert worst > bound / 8, (worst, bound)
