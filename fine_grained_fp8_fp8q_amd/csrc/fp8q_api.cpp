@@ -164,7 +164,8 @@ fp8q_status fp8q_gemm_ex(const uint8_t* a, const float* a_scales, const uint8_t*
   if (!acc_ok(acc)) return FP8Q_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return FP8Q_OK;
   if (fp8q_status st = check_gemm_common(K, out_dtype, c, ld_c, N)) return st;
-  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || tiles256(M, N, 256) >= kMaxGemmTiles)
+  // tiles of 224 or 256 columns: bound the count with the narrower width
+  if (M * K >= kMaxOperandBytes || N * K >= kMaxOperandBytes || tiles256(M, N, 224) >= kMaxGemmTiles)
     return FP8Q_ERR_SHAPE;
   if (K > 0) {
     if (!a || !a_scales || !w || !w_scales) return FP8Q_ERR_INVALID_ARG;

@@ -262,7 +262,10 @@ __device__ __forceinline__ void k_loop3(int nkb, uint8_t* __restrict__ s0, uint8
   }
 }
 
-template <int MODE, int OUT, int ACC>
+// NARROW: tiles of 224 columns (dense and weight-gradient launches whose
+// column count fills the compute units better that way); a kernel of its
+// own, so the 256-column form keeps its registers.
+template <int MODE, int OUT, int ACC, int NARROW>
 __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // two full stages, or (grouped tiles of at most 128 rows) three small
   // ones, then the scale buffer
@@ -319,10 +322,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(t.sw + (size_t)t.n0 * nkb), 0,
                                                (int)((uint32_t)(N - t.n0) * sblk), kRsrcFlags);
     s_off = (uint32_t)sidx * sblk;
-  } else {  // one scale row per 128 columns; n0 is a multiple of 256
+  } else {  // one scale row per 128 columns, from the one holding column n0
     s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(t.sw + (size_t)(t.n0 >> 7) * nkb), 0,
-                                               (int)((uint32_t)((N - t.n0 + 127) >> 7) * sblk), kRsrcFlags);
-    s_off = (uint32_t)(sidx >> 7) * sblk;
+                                               (int)((uint32_t)(((N + 127) >> 7) - (t.n0 >> 7)) * sblk), kRsrcFlags);
+    s_off = 0;  // (unused: these scales arrive by quarters)
   }
   // Scale buffer fill.  Waves 0-3 own A rows 64w..64w+63, waves 4-7 W
   // columns 64(w-4)..+63, laid out [entry][4 blocks] in each half.  One
@@ -336,14 +339,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   // k/128 into zeros.  The weight gradient's W scales (per column and block)
   // go into the block's stage instead, one block per load.  Issued first in
   // a batch.
+  // (the dense and grouped W entries are columns: column e of the tile reads
+  // the scale row of its 128-column block, ((n0 mod 128) + e) / 128 rows past
+  // the buffer's first)
   const int q_entry = (wave & 3) * 64 + (lane >> 2);  // entry of quarter 0
-  const uint32_t q_row = MODE == kWgrad || wave < 4 ? (uint32_t)q_entry : (uint32_t)((wave & 3) >> 1);
-  const uint32_t q_voff = q_row * sblk + 4u * (uint32_t)(lane & 3);
+  const bool row_entries = MODE == kWgrad || wave < 4;
+  const uint32_t q_lane = 4u * (uint32_t)(lane & 3);
+  // (grouped tiles start at a multiple of 256 columns: a W wave's 64
+  // columns share one scale row)
+  const uint32_t q_voff = (row_entries ? (uint32_t)q_entry : (uint32_t)((wave & 3) >> 1)) * sblk + q_lane;
   auto scale_quarter = [&](uint8_t* scl, int grp, int qq) {
     uint8_t* half = scl + (grp & 1) * kSclHalf + (wave < 4 ? 0 : BM * 16) + ((wave & 3) * 64 + 16 * qq) * 16;
-    const uint32_t rows = wave < 4 || MODE == kWgrad ? (uint32_t)(16 * qq) : 0u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)half, 4, q_voff + rows * sblk + (uint32_t)grp * 16u,
-                                             0, 0, 0);
+    uint32_t off;
+    if (MODE == kDense && !row_entries) {
+      off = (uint32_t)(((t.n0 & 127) + q_entry + 16 * qq) >> 7) * sblk + q_lane;
+    } else {
+      off = q_voff + (row_entries ? (uint32_t)(16 * qq) * sblk : 0u);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_void_ptr)half, 4, off + (uint32_t)grp * 16u, 0, 0, 0);
   };
   auto issue_scales = [&](int kb, uint8_t* st, uint8_t* scl, int step) {
     if (MODE == kWgrad && wave >= 4) {
@@ -414,11 +427,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     const int arow0 = wm * 64 + r16;
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa[f] = SA[(arow0 + f * 16) * 4];
-    float sc[4];
+    // Fold scales.  A wave's columns lie in one 128-column block except in
+    // dense tiles of 224 columns (JN = 7), whose 112 columns per wave may
+    // reach into a second block: fragments j < jb (16 columns each, inside
+    // one block) take the first block's weight scale, the others the
+    // second's (sc2).
+    constexpr bool kFragScale = MODE == kDense && JN != 8;
+    float sc[4], sc2[4];
+    const int jb = kFragScale ? (128 - ((t.n0 + wn * WC) & 127)) >> 4 : JN;
     if constexpr (MODE != kWgrad) {
       const float swv = SA[(BM + wn * WC) * 4];
+      const float swv2 = kFragScale ? SA[(BM + wn * WC + WC - 16) * 4] : 0.f;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
+      for (int f = 0; f < 4; ++f) {
+        sc[f] = sa[f] * swv;
+        if constexpr (kFragScale) sc2[f] = sa[f] * swv2;
+      }
     }
     // Wgrad issues the refill later (see below); the other forms once the
     // scales are read
@@ -482,8 +506,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
+        const float s = kFragScale && j >= jb ? sc2[f] : sc[f];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sc[f], acc[f][j][v]);
+        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], s, acc[f][j][v]);
       }
     };
 
@@ -564,7 +589,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     float sa[4], sc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) sa[f] = SA[(arow0 + f * 16) * 4];
+    // (dense tiles of 224 columns: fragments j >= jb take the second
+    // block's weight scale, as in the BF16 form)
+    constexpr bool kFragScale = MODE == kDense && JN != 8;
+    float sc2[4];
+    const int jb = kFragScale ? (128 - ((t.n0 + wn * WC) & 127)) >> 4 : JN;
     const float swv = SA[(BM + wn * WC) * 4];
+    const float swv2 = kFragScale ? SA[(BM + wn * WC + WC - 16) * 4] : 0.f;
     __builtin_amdgcn_sched_barrier(0);
     v4f p[4];
     // Wgrad: column scales of the fragment being folded, read once per
@@ -576,8 +607,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sa[f] * swj[v], acc[f][j][v]);
       } else {
+        const float s = kFragScale && j >= jb ? sc2[f] : sc[f];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], sc[f], acc[f][j][v]);
+        for (int v = 0; v < 4; ++v) acc[f][j][v] = __builtin_fmaf(p[f][v], s, acc[f][j][v]);
       }
     };
 #pragma unroll
@@ -595,7 +627,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
         refill_now();
         if constexpr (MODE != kWgrad) {
 #pragma unroll
-          for (int f = 0; f < 4; ++f) sc[f] = sa[f] * swv;
+          for (int f = 0; f < 4; ++f) {
+            sc[f] = sa[f] * swv;
+            if constexpr (kFragScale) sc2[f] = sa[f] * swv2;
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -809,15 +844,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     } else {
       run(std::integral_constant<int, 2>{});
     }
-  } else if constexpr (MODE == kWgrad) {
+  } else if constexpr (NARROW) {
     // 224-column tiles: the waves split them as 2 x 112 columns (7 W
     // fragments each); the stage still receives 256 W rows (the last 32
     // belong to the next tile and are not used)
-    if (g.bn == 224) {
-      run(std::integral_constant<int, 7>{});
-    } else {
-      run(std::integral_constant<int, 8>{});
-    }
+    static_assert(MODE == kWgrad || (MODE == kDense && (OUT == kOutF32 || OUT == kOutBF16)),
+                  "224-column tiles: dense (float32 / BF16 out) and weight-gradient forms");
+    run(std::integral_constant<int, 7>{});
   } else {
     run(std::integral_constant<int, 8>{});
   }
@@ -839,15 +872,41 @@ int device_cus() {
   return n;
 }
 
+// Tile width in N for a dense or weight-gradient launch.  One tile per CU
+// and round of tiles, so the time goes as (rounds of tiles) x (tile width);
+// 224 columns when that is smaller.  The 2048 x 7168 weight gradient has 224
+// tiles of 256 columns, which leave 32 of 256 CUs idle, or 256 of 224, which
+// fill them; the 4096 x 7168 Dgrad has 448 tiles of 256 (1.75 rounds, two
+// rounds of 256 columns) or 512 of 224 (two rounds of 224 columns).
+int tile_width(int tiles_m, int n) {
+  const int64_t cus = device_cus();
+  auto cost = [&](int bn) {
+    const int64_t tiles = (int64_t)tiles_m * ((n + bn - 1) / bn);
+    return ((tiles + cus - 1) / cus) * bn;
+  };
+  return cost(224) < cost(BN) ? 224 : BN;
+}
+
+template <int MODE, int OUT, int NARROW>
+void launch_acc_w(const GemmArgs& g, int grid, int acc, hipStream_t stream) {
+  if (acc == 2) {
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 2, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);
+  } else if (acc == 1) {
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 1, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 0, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);
+  }
+}
+
 template <int MODE, int OUT>
 hipError_t launch_acc(const GemmArgs& g, int grid, int acc, hipStream_t stream) {
-  if (acc == 2) {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 2>), dim3(grid), dim3(kThreads), 0, stream, g);
-  } else if (acc == 1) {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 1>), dim3(grid), dim3(kThreads), 0, stream, g);
-  } else {
-    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 0>), dim3(grid), dim3(kThreads), 0, stream, g);
+  if constexpr (MODE == kWgrad || (MODE == kDense && (OUT == kOutF32 || OUT == kOutBF16))) {
+    if (g.bn == 224) {
+      launch_acc_w<MODE, OUT, 1>(g, grid, acc, stream);
+      return hipGetLastError();
+    }
   }
+  launch_acc_w<MODE, OUT, 0>(g, grid, acc, stream);
   return hipGetLastError();
 }
 
@@ -860,8 +919,8 @@ hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w
   g.a = a; g.sa = a_scales; g.w = w; g.sw = w_scales; g.offsets = nullptr;
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;
   g.tiles_m = (m + BM - 1) / BM;
-  g.tiles_n = (n + BN - 1) / BN;
-  g.bn = BN;
+  g.bn = tile_width(g.tiles_m, n);
+  g.tiles_n = (n + g.bn - 1) / g.bn;
   const int grid = g.tiles_m * g.tiles_n;
   return bf16_out ? launch_acc<kDense, kOutBF16>(g, grid, acc, stream)
                   : launch_acc<kDense, kOutF32>(g, grid, acc, stream);
@@ -903,16 +962,7 @@ hipError_t launch_wgrad(const uint8_t* dy_t, const float* dy_scales, const uint8
   g.a = dy_t; g.sa = dy_scales; g.w = x_t; g.sw = x_scales; g.offsets = nullptr;
   g.c = dw; g.ldc = lddw; g.vec_c = (lddw % 4) == 0; g.rows = nout; g.n = kin; g.k = t; g.groups = 1;
   g.tiles_m = (nout + BM - 1) / BM;
-  // Tile width: one tile per CU and wave of tiles, so the time goes as
-  // (waves of tiles) x (tile width); 224 columns when that is smaller.  The
-  // 2048 x 7168 weight gradient has 224 tiles of 256 columns, which leave 32
-  // of 256 CUs idle, or 256 of 224, which fill them.
-  const int64_t cus = device_cus();
-  auto cost = [&](int bn) {
-    const int64_t tiles = (int64_t)g.tiles_m * ((kin + bn - 1) / bn);
-    return ((tiles + cus - 1) / cus) * bn;
-  };
-  g.bn = cost(224) < cost(BN) ? 224 : BN;
+  g.bn = tile_width(g.tiles_m, kin);
   g.tiles_n = (kin + g.bn - 1) / g.bn;
   return launch_acc<kWgrad, kOutF32>(g, g.tiles_m * g.tiles_n, acc, stream);
 }

@@ -15,7 +15,30 @@ namespace fp8q {
 // A 16-lane DPP row owns one tile (16 lanes x 8 BF16).  Each wave handles
 // 16 consecutive tiles per iteration: load u (0..3) of lane l reads tile
 // base + 4u + l/16, so every load instruction covers 4 consecutive tiles
-// (1 KiB when they share a row).
+// (1 KiB when they share a row).  The scales of a DPP row's four tiles are
+// worked out once, lane u of the row taking tile u, and broadcast back to
+// the row (row_newbcast): one scale computation per lane and iteration
+// instead of four (the free scale is two IEEE divisions).
+
+// Tile u's scale state, from lane u of each DPP row.
+template <bool POW2, int U>
+__device__ __forceinline__ TileScale row_tile_scale(const TileScale& tm) {
+  TileScale ts;
+  ts.s = 0.0f;  // (stored by lane u itself)
+  if constexpr (POW2) {
+    ts.div = 1.0f;
+    ts.mul = 1.0f;
+    ts.slow = false;
+    ts.neg_e = (int)row_bcast<U>((uint32_t)tm.neg_e);
+  } else {
+    ts.div = row_bcast<U>(tm.div);
+    ts.mul = row_bcast<U>(tm.mul);
+    ts.neg_e = 0;
+    ts.slow = row_bcast<U>((uint32_t)tm.slow) != 0u;
+  }
+  return ts;
+}
+
 template <bool POW2>
 __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint16_t* __restrict__ x, int cols,
                                                 int64_t ldx, uint8_t* __restrict__ codes, int64_t ldc,
@@ -32,12 +55,28 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
     uint4 v[4];
     int row[4], cb[4];
     bool valid[4], full[4];
+    // tile base + 4u + grp is (row[u], cb[u]): one division, then steps of
+    // four tiles (rows of at least four tiles) or a division per tile
+    {
+      const uint32_t t = base + (uint32_t)grp;
+      row[0] = (int)(t / (uint32_t)nb);
+      cb[0] = (int)(t - (uint32_t)row[0] * (uint32_t)nb);
+    }
+#pragma unroll
+    for (int u = 1; u < 4; ++u) {
+      if (nb >= 4) {
+        const bool wrap = cb[u - 1] + 4 >= nb;
+        cb[u] = cb[u - 1] + 4 - (wrap ? nb : 0);
+        row[u] = row[u - 1] + (wrap ? 1 : 0);
+      } else {
+        const uint32_t t = base + (uint32_t)(4 * u + grp);
+        row[u] = (int)(t / (uint32_t)nb);
+        cb[u] = (int)(t - (uint32_t)row[u] * (uint32_t)nb);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const uint32_t t = base + (uint32_t)(u * 4 + grp);
-      valid[u] = t < (uint32_t)ntiles;
-      row[u] = valid[u] ? (int)(t / (uint32_t)nb) : 0;
-      cb[u] = valid[u] ? (int)(t - (uint32_t)row[u] * (uint32_t)nb) : 0;
+      valid[u] = base + (uint32_t)(u * 4 + grp) < (uint32_t)ntiles;
       full[u] = vec && valid[u] && (cb[u] * 128 + 128 <= cols);
       const uint16_t* src = x + (int64_t)row[u] * ldx + cb[u] * 128 + sub * 8;
       if (full[u]) {
@@ -46,10 +85,18 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
         v[u] = load8_masked(src, valid[u] ? cols - (cb[u] * 128 + sub * 8) : 0);
       }
     }
+    uint32_t am[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t amax = dpp_max16(absmax8(v[u]));
-      const TileScale ts = tile_scale<POW2>(amax);
+    for (int u = 0; u < 4; ++u) am[u] = dpp_max16(absmax8(v[u]));
+    // lane u (< 4) of each DPP row takes the row's tile u; the scale matrix
+    // is [rows, nb] contiguous, so tile t's scale is scales[t]
+    const uint32_t mine = sub == 1 ? am[1] : sub == 2 ? am[2] : sub == 3 ? am[3] : am[0];
+    const TileScale tm = tile_scale<POW2>(mine);
+    {
+      const uint32_t ts_tile = base + (uint32_t)(4 * sub + grp);
+      if (sub < 4 && ts_tile < (uint32_t)ntiles) scales[ts_tile] = tm.s;
+    }
+    auto encode_store = [&](int u, const TileScale& ts) {
       const uint2 c = encode8<POW2>(v[u], ts);
       uint8_t* dst = codes + (int64_t)row[u] * ldc + cb[u] * 128 + sub * 8;
       if (full[u]) {
@@ -57,8 +104,11 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
       } else if (valid[u]) {
         store8_masked(dst, c, cols - (cb[u] * 128 + sub * 8));
       }
-      if (sub == 0 && valid[u]) scales[(int64_t)row[u] * nb + cb[u]] = ts.s;
-    }
+    };
+    encode_store(0, row_tile_scale<POW2, 0>(tm));
+    encode_store(1, row_tile_scale<POW2, 1>(tm));
+    encode_store(2, row_tile_scale<POW2, 2>(tm));
+    encode_store(3, row_tile_scale<POW2, 3>(tm));
   }
 }
 

@@ -182,15 +182,48 @@ __device__ __forceinline__ auto with_quotient(const TileScale& t, Body body) {
   }
 }
 
-// Eight BF16 values (one 16-byte chunk) -> eight codes (two words).
+// The sign bits of four BF16 values (words a, b: low half first) as the
+// sign bits of four code bytes, in pack4_e4m3's order.
+__device__ __forceinline__ uint32_t signs4(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07050301u) & 0x80808080u;
+}
+
+// Eight BF16 values (one 16-byte chunk) -> eight codes (two words).  In the
+// common free-scale case the Markstein quotient goes without its copysign:
+// it already carries the sign of every nonzero input, and OR-ing the inputs'
+// sign bits into the codes restores the one it loses, that of -0 (+0 / s
+// and -0 / s both come out +0).
 template <bool POW2>
 __device__ __forceinline__ uint2 encode8(uint4 v, const TileScale& t) {
+  if constexpr (!POW2) {
+    if (__builtin_amdgcn_ballot_w64(t.slow) == 0) {
+      auto q = [&](float x) {
+        const float q0 = x * t.mul;
+        const float e = __builtin_fmaf(-q0, t.div, x);
+        return __builtin_fmaf(e, t.mul, q0);
+      };
+      uint2 r;
+      r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y))) | signs4(v.x, v.y);
+      r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w))) | signs4(v.z, v.w);
+      return r;
+    }
+  }
   return with_quotient<POW2>(t, [&](auto q) {
     uint2 r;
     r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
     r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
     return r;
   });
+}
+
+// Lane n of each 16-lane DPP row, broadcast to the row (row_newbcast).
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+}
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __uint_as_float(row_bcast<N>(__float_as_uint(v)));
 }
 
 // Loads up to 8 BF16 values (nvalid may be <= 0 or >= 8); missing ones are +0.

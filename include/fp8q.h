@@ -169,8 +169,9 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
  * stride ld_c elements.  C is overwritten.  Partials are formed at float32
  * grade (FP8Q_ACC_FP32): |C - exact| <= 1e-5 * sum|a*b| + 1e-6.
  * Each code operand is below 2 GiB, and fewer than 2^23 output tiles of
- * 256 x 256 (one workgroup each; for the grouped and weight-gradient forms
- * the tile counts they launch), else FP8Q_ERR_SHAPE. */
+ * 256 x 224 (one workgroup each: tiles are 256 or 224 columns wide,
+ * whichever fills the compute units in fewer column-widths; for the grouped
+ * form the tile count it launches), else FP8Q_ERR_SHAPE. */
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       const uint8_t* w, const float* w_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype,
