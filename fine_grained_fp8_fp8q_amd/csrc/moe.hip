@@ -82,16 +82,19 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return (g * sg) * u;
 }
 
-// Eight (gate, up) BF16 pairs -> eight BF16 SwiGLU values in chunk layout.
+// Eight (gate, up) BF16 pairs -> eight BF16 SwiGLU values in chunk layout,
+// each rounded to nearest even by the hardware convert (v_cvt_pk_bf16_f32,
+// two values per instruction).
+typedef __bf16 sw_v2bf __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
   const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
   const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
   uint32_t y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = bf16_rne_bits(swiglu(bf16_lo(gw[i]), bf16_lo(uw[i])));
-    const uint32_t hi = bf16_rne_bits(swiglu(bf16_hi(gw[i]), bf16_hi(uw[i])));
-    y[i] = lo | (hi << 16);
+    const float lo = swiglu(bf16_lo(gw[i]), bf16_lo(uw[i]));
+    const float hi = swiglu(bf16_hi(gw[i]), bf16_hi(uw[i]));
+    y[i] = __builtin_bit_cast(uint32_t, sw_v2bf{(__bf16)lo, (__bf16)hi});
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
 }
@@ -113,12 +116,11 @@ __device__ __forceinline__ void quant_store(uint4 v, bool full, bool valid, int 
 }
 
 // A 16-lane DPP row owns one output tile (128 columns of inter): lane sub
-// reads 8 gate and 8 up values.  Each wave covers 4 * kSwU tiles per
-// iteration (load u of lane l: tile base + 4u + l/16), all loads first.
-// The kernel is bound by its float32 arithmetic as much as by HBM; one
-// tile per DPP row and iteration (more waves, each with less in flight)
-// measured fastest (3773 x 2048 outputs: 11.3 us against 13.9 us with four).
-constexpr int kSwU = 1;
+// reads 8 gate and 8 up values.  Each wave covers 4 tiles per iteration
+// (lane l: tile base + l/16) of a grid-stride loop and loads the next
+// iteration's gate and up chunks before it works on the current ones: the
+// kernel is bound by its float32 arithmetic as much as by HBM, and the next
+// loads stay in flight through that arithmetic.
 template <bool POW2, bool CACHE, bool CPOW2>
 __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __restrict__ x, int inter, int64_t ldx,
                                                            uint8_t* __restrict__ codes, int64_t ldc,
@@ -129,47 +131,54 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
   const int grp = lane >> 4;
   const int sub = lane & 15;
   // 32-bit unsigned tile indices: ntiles < 2^31 and the stride is at most
-  // 4 * kSwU * 4 * kMaxStreamGrid, so base + stride never wraps.
+  // 4 * 4 * kMaxStreamGrid, so base + stride never wraps.
   const uint32_t wave = (blockIdx.x * 256u + threadIdx.x) >> 6;
-  const uint32_t step = gridDim.x * 16u * kSwU;
+  const uint32_t step = gridDim.x * 16u;
 
-  for (uint32_t base = wave * 4u * kSwU; base < (uint32_t)ntiles; base += step) {
-    uint4 gv[kSwU], uv[kSwU];
-    int row[kSwU], col[kSwU], nvalid[kSwU];
-    bool valid[kSwU], full[kSwU];
-#pragma unroll
-    for (int u = 0; u < kSwU; ++u) {
-      const uint32_t t = base + (uint32_t)(u * 4 + grp);
-      valid[u] = t < (uint32_t)ntiles;
-      row[u] = valid[u] ? (int)(t / (uint32_t)nb) : 0;
-      const int cb = valid[u] ? (int)(t - (uint32_t)row[u] * (uint32_t)nb) : 0;
-      col[u] = cb * 128 + sub * 8;
-      nvalid[u] = valid[u] ? inter - col[u] : 0;
-      full[u] = vec && valid[u] && (cb * 128 + 128 <= inter);
-      const uint16_t* src = x + (int64_t)row[u] * ldx + col[u];
-      if (full[u]) {
-        gv[u] = ld_stream16(src);
-        uv[u] = ld_stream16(src + inter);
-      } else {
-        gv[u] = load8_masked(src, nvalid[u]);
-        uv[u] = load8_masked(src + inter, nvalid[u]);
-      }
+  struct Chunk {
+    uint4 g, u;
+    int row, col, nvalid;
+    bool valid, full;
+  };
+  auto fetch = [&](uint32_t base, Chunk& c) {
+    const uint32_t t = base + (uint32_t)grp;
+    c.valid = t < (uint32_t)ntiles;
+    c.row = c.valid ? (int)(t / (uint32_t)nb) : 0;
+    const int cb = c.valid ? (int)(t - (uint32_t)c.row * (uint32_t)nb) : 0;
+    c.col = cb * 128 + sub * 8;
+    c.nvalid = c.valid ? inter - c.col : 0;
+    c.full = vec && c.valid && (cb * 128 + 128 <= inter);
+    const uint16_t* src = x + (int64_t)c.row * ldx + c.col;
+    if (c.full) {
+      c.g = ld_stream16(src);
+      c.u = ld_stream16(src + inter);
+    } else {
+      c.g = load8_masked(src, c.nvalid);
+      c.u = load8_masked(src + inter, c.nvalid);
     }
-#pragma unroll
-    for (int u = 0; u < kSwU; ++u) {
-      const int cb = col[u] >> 7;
-      const uint4 y = swiglu8(gv[u], uv[u]);
-      quant_store<POW2>(y, full[u], valid[u], nvalid[u], codes + (int64_t)row[u] * ldc + col[u],
-                        scales + (int64_t)row[u] * nb + cb, sub);
-      if constexpr (CACHE) {
-        // inter is a multiple of 128 here: the gate chunk is input tile cb,
-        // the up chunk input tile nb + cb of the same row
-        uint8_t* cdst = ccodes + (int64_t)row[u] * ldcc + col[u];
-        float* sdst = cscales + (int64_t)row[u] * (2 * nb) + cb;
-        quant_store<CPOW2>(gv[u], full[u], valid[u], nvalid[u], cdst, sdst, sub);
-        quant_store<CPOW2>(uv[u], full[u], valid[u], nvalid[u], cdst + inter, sdst + nb, sub);
-      }
+  };
+
+  uint32_t base = wave * 4u;
+  if (base >= (uint32_t)ntiles) return;  // (wave-uniform)
+  Chunk cur;
+  fetch(base, cur);
+  for (; base < (uint32_t)ntiles; base += step) {
+    Chunk nxt = cur;
+    const uint32_t nbase = base + step;
+    if (nbase < (uint32_t)ntiles) fetch(nbase, nxt);  // (wave-uniform)
+    const int cb = cur.col >> 7;
+    const uint4 y = swiglu8(cur.g, cur.u);
+    quant_store<POW2>(y, cur.full, cur.valid, cur.nvalid, codes + (int64_t)cur.row * ldc + cur.col,
+                      scales + (int64_t)cur.row * nb + cb, sub);
+    if constexpr (CACHE) {
+      // inter is a multiple of 128 here: the gate chunk is input tile cb,
+      // the up chunk input tile nb + cb of the same row
+      uint8_t* cdst = ccodes + (int64_t)cur.row * ldcc + cur.col;
+      float* sdst = cscales + (int64_t)cur.row * (2 * nb) + cb;
+      quant_store<CPOW2>(cur.g, cur.full, cur.valid, cur.nvalid, cdst, sdst, sub);
+      quant_store<CPOW2>(cur.u, cur.full, cur.valid, cur.nvalid, cdst + inter, sdst + nb, sub);
     }
+    cur = nxt;
   }
 }
 
@@ -181,7 +190,7 @@ hipError_t launch_swiglu(const uint16_t* x, int rows, int inter, int64_t ldx, ui
   const int nb = (inter + 127) / 128;
   const int ntiles = rows * nb;  // < 2^31 (checked by the entry point)
   const bool vec = (ldx % 8 == 0) && (inter % 8 == 0) && (ldc % 8 == 0) && (!CACHE || ldcc % 8 == 0);
-  const int64_t waves = ((int64_t)ntiles + 4 * kSwU - 1) / (4 * kSwU);
+  const int64_t waves = ((int64_t)ntiles + 3) / 4;
   hipLaunchKernelGGL((swiglu_quant_kernel<POW2, CACHE, CPOW2>), dim3(stream_grid(waves)), dim3(256), 0, stream, x,
                      inter, ldx, codes, ldc, scales, ccodes, ldcc, cscales, nb, ntiles, vec);
   return hipGetLastError();
