@@ -339,9 +339,12 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
                                                             bool vec) {
   constexpr int kRowBytes = 144;  // 16-byte aligned rows for the store reads
   __shared__ uint32_t red[4][64];
-  __shared__ float s_div[64], s_mul[64];
-  __shared__ int s_nege[64];
+  // per-feature scale state, read back 8 features (32 bytes) at a time
+  __shared__ __attribute__((aligned(16))) float s_div[64];
+  __shared__ __attribute__((aligned(16))) float s_mul[64];
+  __shared__ __attribute__((aligned(16))) int s_nege[64];
   __shared__ unsigned char s_slow[64];
+  __shared__ int s_anyslow;  // some feature of the block takes the IEEE division
   __shared__ __attribute__((aligned(16))) uint8_t tile[64 * kRowBytes];
 
   const int tid = threadIdx.x;
@@ -373,13 +376,15 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
   m[1] = pk_max_u16(pk_max_u16(v[0].y & k, v[1].y & k), pk_max_u16(v[2].y & k, v[3].y & k));
   m[2] = pk_max_u16(pk_max_u16(v[0].z & k, v[1].z & k), pk_max_u16(v[2].z & k, v[3].z & k));
   m[3] = pk_max_u16(pk_max_u16(v[0].w & k, v[1].w & k), pk_max_u16(v[2].w & k, v[3].w & k));
-  // across the 8 lanes of the wave with the same c8 (lane bits 3..5)
+  // across the 8 lanes of the wave with the same c8 (lane bits 3..5):
+  // lane l ^ 8 is lane l rotated by 8 within its 16-lane DPP row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    m[i] = pk_max_u16(m[i], (uint32_t)__shfl_xor((int)m[i], 8));
+    m[i] = pk_max_u16(m[i], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m[i], 0x128, 0xF, 0xF, false));
     m[i] = pk_max_u16(m[i], (uint32_t)__shfl_xor((int)m[i], 16));
     m[i] = pk_max_u16(m[i], (uint32_t)__shfl_xor((int)m[i], 32));
   }
+  if (tid == 0) s_anyslow = 0;
   if (lane < 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -395,27 +400,75 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
     s_mul[tid] = ts.mul;
     s_nege[tid] = ts.neg_e;
     s_slow[tid] = ts.slow;
+    if (ts.slow) s_anyslow = 1;
     if (f0 + tid < cols) scales[(int64_t)(f0 + tid) * ntb + tb] = ts.s;
   }
   __syncthreads();
 
-  // encode: feature 8*c8 + j, tokens 4q..4q+3 -> one word at tile[f][4q]
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  // encode: feature 8*c8 + j, tokens 4q..4q+3 -> one word at tile[f][4q].
+  // The thread's 8 features' scale state comes in as whole 16-byte LDS
+  // reads; the per-element IEEE division of a tiny-amax feature is taken
+  // only when the block has one (a workgroup-uniform branch), so the common
+  // case is the bare Markstein quotient with no per-element branch.
+  auto word_of = [&](int p, int j) {
+    return (j >> 1) == 0 ? v[p].x : (j >> 1) == 1 ? v[p].y : (j >> 1) == 2 ? v[p].z : v[p].w;
+  };
+  auto put = [&](int j, uint32_t w) {
     const int f = 8 * c8 + j;
-    TileScale ts;
-    ts.div = s_div[f];
-    ts.mul = s_mul[f];
-    ts.neg_e = s_nege[f];
-    ts.slow = s_slow[f] != 0;
-    float e[4];
+    *reinterpret_cast<uint32_t*>(&tile[f * kRowBytes + 4 * ((q + 8 * c8) & 31)]) = w;
+  };
+  if constexpr (POW2) {
+    const int4 n0 = *reinterpret_cast<const int4*>(&s_nege[8 * c8]);
+    const int4 n1 = *reinterpret_cast<const int4*>(&s_nege[8 * c8 + 4]);
+    const int ne[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t word = (j >> 1) == 0 ? v[p].x : (j >> 1) == 1 ? v[p].y : (j >> 1) == 2 ? v[p].z : v[p].w;
-      e[p] = quotient<POW2>((j & 1) ? bf16_hi(word) : bf16_lo(word), ts);
+    for (int j = 0; j < 8; ++j) {
+      float e[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t word = word_of(p, j);
+        e[p] = __builtin_ldexpf((j & 1) ? bf16_hi(word) : bf16_lo(word), ne[j]);
+      }
+      put(j, pack4_e4m3(e[0], e[1], e[2], e[3]));
     }
-    *reinterpret_cast<uint32_t*>(&tile[f * kRowBytes + 4 * ((q + 8 * c8) & 31)]) =
-        pack4_e4m3(e[0], e[1], e[2], e[3]);
+  } else {
+    const float4 d0 = *reinterpret_cast<const float4*>(&s_div[8 * c8]);
+    const float4 d1 = *reinterpret_cast<const float4*>(&s_div[8 * c8 + 4]);
+    const float4 r0 = *reinterpret_cast<const float4*>(&s_mul[8 * c8]);
+    const float4 r1 = *reinterpret_cast<const float4*>(&s_mul[8 * c8 + 4]);
+    const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    const float ml[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    if (s_anyslow == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float e[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t word = word_of(p, j);
+          const float xv = (j & 1) ? bf16_hi(word) : bf16_lo(word);
+          const float q0 = xv * ml[j];
+          const float er = __builtin_fmaf(-q0, dv[j], xv);
+          e[p] = __builtin_copysignf(__builtin_fmaf(er, ml[j], q0), xv);
+        }
+        put(j, pack4_e4m3(e[0], e[1], e[2], e[3]));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        TileScale ts;
+        ts.div = dv[j];
+        ts.mul = ml[j];
+        ts.neg_e = 0;
+        ts.slow = s_slow[8 * c8 + j] != 0;
+        float e[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t word = word_of(p, j);
+          e[p] = quotient_free((j & 1) ? bf16_hi(word) : bf16_lo(word), ts);
+        }
+        put(j, pack4_e4m3(e[0], e[1], e[2], e[3]));
+      }
+    }
   }
   __syncthreads();
 
