@@ -6,6 +6,8 @@
 // write of the FP8 values back; the kernels below make that round trip at
 // close to HBM speed: one 16-byte load per lane per 8 elements, a DPP
 // max-abs over the 16 lanes that hold one tile, and packed code stores.
+#include <type_traits>
+
 #include "fp8q_internal.h"
 #include "quant_common.h"
 
@@ -28,6 +30,7 @@ __device__ __forceinline__ TileScale row_tile_scale(const TileScale& tm) {
   if constexpr (POW2) {
     ts.div = 1.0f;
     ts.mul = 1.0f;
+    ts.xscale = 1.0f;
     ts.slow = false;
     ts.neg_e = (int)row_bcast<U>((uint32_t)tm.neg_e);
   } else {
@@ -35,6 +38,7 @@ __device__ __forceinline__ TileScale row_tile_scale(const TileScale& tm) {
     ts.mul = row_bcast<U>(tm.mul);
     ts.neg_e = 0;
     ts.slow = row_bcast<U>((uint32_t)tm.slow) != 0u;
+    ts.xscale = ts.slow ? 0x1p64f : 1.0f;
   }
   return ts;
 }
@@ -96,8 +100,8 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
       const uint32_t ts_tile = base + (uint32_t)(4 * sub + grp);
       if (sub < 4 && ts_tile < (uint32_t)ntiles) scales[ts_tile] = tm.s;
     }
-    auto encode_store = [&](int u, const TileScale& ts) {
-      const uint2 c = encode8<POW2>(v[u], ts);
+    auto encode_store = [&](int u, const TileScale& ts, auto enc) {
+      const uint2 c = enc(v[u], ts);
       uint8_t* dst = codes + (int64_t)row[u] * ldc + cb[u] * 128 + sub * 8;
       if (full[u]) {
         st_stream8(dst, c);
@@ -105,10 +109,20 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
         store8_masked(dst, c, cols - (cb[u] * 128 + sub * 8));
       }
     };
-    encode_store(0, row_tile_scale<POW2, 0>(tm));
-    encode_store(1, row_tile_scale<POW2, 1>(tm));
-    encode_store(2, row_tile_scale<POW2, 2>(tm));
-    encode_store(3, row_tile_scale<POW2, 3>(tm));
+    auto all4 = [&](auto enc) {
+      encode_store(0, row_tile_scale<POW2, 0>(tm), enc);
+      encode_store(1, row_tile_scale<POW2, 1>(tm), enc);
+      encode_store(2, row_tile_scale<POW2, 2>(tm), enc);
+      encode_store(3, row_tile_scale<POW2, 3>(tm), enc);
+    };
+    if constexpr (POW2) {
+      all4([](uint4 x, const TileScale& t) { return encode8<true>(x, t); });
+    } else if (__builtin_amdgcn_ballot_w64(sub < 4 && tm.slow) == 0) {
+      // (one wave-uniform decision for the wave's 16 tiles)
+      all4([](uint4 x, const TileScale& t) { return encode8_markstein<false>(x, t); });
+    } else {
+      all4([](uint4 x, const TileScale& t) { return encode8_markstein<true>(x, t); });
+    }
   }
 }
 
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
   __shared__ __attribute__((aligned(16))) float s_mul[64];
   __shared__ __attribute__((aligned(16))) int s_nege[64];
   __shared__ unsigned char s_slow[64];
-  __shared__ int s_anyslow;  // some feature of the block takes the IEEE division
+  __shared__ int s_anyslow;  // some feature of the block has a tiny amax
   __shared__ __attribute__((aligned(16))) uint8_t tile[64 * kRowBytes];
 
   const int tid = threadIdx.x;
@@ -407,9 +421,9 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
 
   // encode: feature 8*c8 + j, tokens 4q..4q+3 -> one word at tile[f][4q].
   // The thread's 8 features' scale state comes in as whole 16-byte LDS
-  // reads; the per-element IEEE division of a tiny-amax feature is taken
-  // only when the block has one (a workgroup-uniform branch), so the common
-  // case is the bare Markstein quotient with no per-element branch.
+  // reads; the scaling of x by 2^64 for a tiny-amax feature is taken only
+  // when the block has one (a workgroup-uniform branch), so the common case
+  // is the bare Markstein quotient.
   auto word_of = [&](int p, int j) {
     return (j >> 1) == 0 ? v[p].x : (j >> 1) == 1 ? v[p].y : (j >> 1) == 2 ? v[p].z : v[p].w;
   };
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
     const float4 r1 = *reinterpret_cast<const float4*>(&s_mul[8 * c8 + 4]);
     const float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
     const float ml[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    if (s_anyslow == 0) {
+    if (s_anyslow == 0) {  // (workgroup-uniform)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float e[4];
@@ -453,6 +467,7 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
         put(j, pack4_e4m3(e[0], e[1], e[2], e[3]));
       }
     } else {
+      // a tiny-amax feature scales its x by 2^64 (its divisor already is)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         TileScale ts;
@@ -460,6 +475,7 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
         ts.mul = ml[j];
         ts.neg_e = 0;
         ts.slow = s_slow[8 * c8 + j] != 0;
+        ts.xscale = ts.slow ? 0x1p64f : 1.0f;
         float e[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -467,6 +483,9 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
           e[p] = quotient_free((j & 1) ? bf16_hi(word) : bf16_lo(word), ts);
         }
         put(j, pack4_e4m3(e[0], e[1], e[2], e[3]));
+        // (one feature at a time: this rare path keeps the fast path's
+        // register budget)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fp8q {
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -77,15 +79,19 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 // is RN32(x/s) computed with one Markstein correction (M. Markstein, IBM J.
 // Res. Dev. 34(1), 1990): q0 = x*r, e = fma(-q0, s, x), q = fma(e, r, q0).
 // For BF16 x and amax >= 2^-90 this equals the IEEE quotient for every pair
-// whose quotient is >= 2^-10 (smaller quotients encode to zero either way);
-// below that amax the tile takes the IEEE division per element.  For
-// power-of-two scales the quotient is an exact ldexp.
+// whose quotient is >= 2^-10 (smaller quotients encode to zero either way).
+// A tile with a smaller (nonzero) amax scales x and s by 2^64 first (exact;
+// x' / s' = x / s), and the same three steps on (x', s') equal the IEEE
+// quotient for every such pair.  Both claims are checked on the host over
+// every BF16 (x, amax) pair.  For power-of-two scales the quotient is an
+// exact ldexp.
 struct TileScale {
-  float s;     // the scale written out (0 for an all-zero tile)
-  float div;   // divisor used for the quotient (1 for a zero tile)
-  float mul;   // RN32(1 / div)
-  int neg_e;   // pow2: -e
-  bool slow;   // free scales with a tiny amax: per-element IEEE division
+  float s;       // the scale written out (0 for an all-zero tile)
+  float div;     // divisor used for the quotient: s, s * 2^64 for a tiny tile, 1 for a zero tile
+  float mul;     // RN32(1 / div)
+  float xscale;  // x is multiplied by this first: 2^64 for a tiny tile, else 1
+  int neg_e;     // pow2: -e
+  bool slow;     // free scales with a tiny amax: x and s scaled by 2^64
 };
 
 constexpr uint32_t kMarksteinMinAmaxBits = 37u << 7;  // BF16 pattern of 2^-90
@@ -95,10 +101,11 @@ __device__ __forceinline__ TileScale tile_scale_free(uint32_t amax_bits) {
   float amax = __uint_as_float(amax_bits << 16);
   float s = amax / 448.0f;  // IEEE division (no fast-math)
   t.s = s;
-  t.div = amax_bits ? s : 1.0f;
+  t.slow = amax_bits != 0 && amax_bits < kMarksteinMinAmaxBits;
+  t.xscale = t.slow ? 0x1p64f : 1.0f;
+  t.div = amax_bits ? s * t.xscale : 1.0f;
   t.mul = 1.0f / t.div;
   t.neg_e = 0;
-  t.slow = amax_bits != 0 && amax_bits < kMarksteinMinAmaxBits;
   return t;
 }
 
@@ -107,6 +114,7 @@ __device__ __forceinline__ TileScale tile_scale_pow2(uint32_t amax_bits) {
   t.slow = false;
   t.div = 1.0f;
   t.mul = 1.0f;
+  t.xscale = 1.0f;
   if (amax_bits == 0) {
     t.s = 0.0f;
     t.neg_e = 0;
@@ -132,15 +140,10 @@ __device__ __forceinline__ TileScale tile_scale_pow2(uint32_t amax_bits) {
 }
 
 __device__ __forceinline__ float quotient_free(float x, const TileScale& t) {
-  float q;
-  if (t.slow) {
-    q = x / t.div;
-  } else {
-    float q0 = x * t.mul;
-    float e = __builtin_fmaf(-q0, t.div, x);
-    q = __builtin_fmaf(e, t.mul, q0);
-  }
-  return __builtin_copysignf(q, x);  // keeps -0 for negative zero inputs
+  const float xs = x * t.xscale;
+  const float q0 = xs * t.mul;
+  const float e = __builtin_fmaf(-q0, t.div, xs);
+  return __builtin_copysignf(__builtin_fmaf(e, t.mul, q0), x);  // keeps -0 for negative zero inputs
 }
 
 template <bool POW2>
@@ -162,10 +165,10 @@ __device__ __forceinline__ TileScale tile_scale(uint32_t amax_bits) {
 }
 
 // Runs body(q) with q(x) = the tile quotient of x.  Free scales: the
-// per-element IEEE division of a tiny-amax tile is taken only when some lane
-// of the wave holds such a tile (a wave-uniform branch: call it with every
-// lane of the wave active), so the common case is the bare Markstein
-// quotient with no per-element branching.
+// multiplication of x by 2^64 for a tiny-amax tile is taken only when some
+// lane of the wave holds such a tile (a wave-uniform branch: call it with
+// every lane of the wave active), so the common case is the bare Markstein
+// quotient.
 template <bool POW2, class Body>
 __device__ __forceinline__ auto with_quotient(const TileScale& t, Body body) {
   if constexpr (POW2) {
@@ -188,32 +191,43 @@ __device__ __forceinline__ uint32_t signs4(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07050301u) & 0x80808080u;
 }
 
-// Eight BF16 values (one 16-byte chunk) -> eight codes (two words).  In the
-// common free-scale case the Markstein quotient goes without its copysign:
-// it already carries the sign of every nonzero input, and OR-ing the inputs'
-// sign bits into the codes restores the one it loses, that of -0 (+0 / s
-// and -0 / s both come out +0).
+// Eight BF16 values (one 16-byte chunk) -> eight codes (two words), free
+// scales.  The Markstein quotient goes without its copysign: it already
+// carries the sign of every nonzero input, and OR-ing the inputs' sign bits
+// into the codes restores the one it loses, that of -0 (+0 / s and -0 / s
+// both come out +0).  SCALED: x is first multiplied by the tile's xscale
+// (2^64 for a tiny-amax tile, else 1); without it the caller has checked
+// that no tile of its wave is tiny.
+template <bool SCALED>
+__device__ __forceinline__ uint2 encode8_markstein(uint4 v, const TileScale& t) {
+  auto q = [&](float x) {
+    const float xs = SCALED ? x * t.xscale : x;
+    const float q0 = xs * t.mul;
+    const float e = __builtin_fmaf(-q0, t.div, xs);
+    return __builtin_fmaf(e, t.mul, q0);
+  };
+  uint2 r;
+  r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y))) | signs4(v.x, v.y);
+  r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w))) | signs4(v.z, v.w);
+  return r;
+}
+
+// Eight BF16 values -> eight codes.  Free scales: the multiplication by 2^64
+// of a tiny-amax tile is taken only when some lane of the wave holds such a
+// tile (a wave-uniform branch: call it with every lane of the wave active).
 template <bool POW2>
 __device__ __forceinline__ uint2 encode8(uint4 v, const TileScale& t) {
-  if constexpr (!POW2) {
-    if (__builtin_amdgcn_ballot_w64(t.slow) == 0) {
-      auto q = [&](float x) {
-        const float q0 = x * t.mul;
-        const float e = __builtin_fmaf(-q0, t.div, x);
-        return __builtin_fmaf(e, t.mul, q0);
-      };
+  if constexpr (POW2) {
+    return with_quotient<true>(t, [&](auto q) {
       uint2 r;
-      r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y))) | signs4(v.x, v.y);
-      r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w))) | signs4(v.z, v.w);
+      r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
+      r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
       return r;
-    }
+    });
+  } else {
+    if (__builtin_amdgcn_ballot_w64(t.slow) == 0) return encode8_markstein<false>(v, t);
+    return encode8_markstein<true>(v, t);
   }
-  return with_quotient<POW2>(t, [&](auto q) {
-    uint2 r;
-    r.x = pack4_e4m3(q(bf16_lo(v.x)), q(bf16_hi(v.x)), q(bf16_lo(v.y)), q(bf16_hi(v.y)));
-    r.y = pack4_e4m3(q(bf16_lo(v.z)), q(bf16_hi(v.z)), q(bf16_lo(v.w)), q(bf16_hi(v.w)));
-    return r;
-  });
 }
 
 // Lane n of each 16-lane DPP row, broadcast to the row (row_newbcast).

@@ -1,12 +1,12 @@
 """Exhaustive host check of the quantizers' element quotient (CPU).
 
 The GPU quantizers replace the per-element IEEE division x / s by one
-Markstein correction of x * RN32(1/s) (three float32 operations).  The C
-program tests/host/markstein_check.c runs that sequence and the IEEE
-division on every pair of BF16 values (amax >= 2^-90, |x| <= amax; 521
-million pairs) and requires equal quotients, or both at most 2^-10 (both
-then encode to the E4M3 zero).  Below amax = 2^-90 the kernels divide per
-element; that branch is covered by the GPU tests' tiny-amax tiles.
+Markstein correction of x * RN32(1/s) (three float32 operations); a tile
+with 0 < amax < 2^-90 first scales x and s by 2^64.  The C program
+tests/host/markstein_check.c runs both sequences and the IEEE division on
+every pair of BF16 values with |x| <= amax (521 million pairs with amax >=
+2^-90, 11.2 million below) and requires equal quotients, or both at most
+2^-10 (both then encode to the E4M3 zero).
 """
 
 import os
@@ -34,3 +34,4 @@ def test_markstein_quotient_equals_ieee_division_for_every_bf16_pair(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=600)
     assert run.returncode == 0, run.stdout[-2000:]
     assert "pairs 521483904" in run.stdout and "mismatches 0" in run.stdout, run.stdout
+    assert "tiny pairs 11217215 equal 11217215" in run.stdout and "tiny pairs" in run.stdout, run.stdout
