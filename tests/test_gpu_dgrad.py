@@ -12,7 +12,7 @@ quantization of W (both scale modes, ragged shapes, with and without the
 plain copy); dX within |gpu - oracle| <= 1e-5 * S + 1e-6 (BF16: the interval
 rule) every element at small sizes and sampled at the up-projection's
 gradient shape (dY 4096 x 4096, W 4096 x 7168); the FP8-unit mode against
-the oracle's model of that unit.
+the hardware model of that unit (tests/fp8_unit_model.py, no parity claim).
 """
 
 import numpy as np

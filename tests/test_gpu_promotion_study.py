@@ -7,7 +7,7 @@ dW = dY^T X over 16384 tokens (dY 16384 x 2048, X 16384 x 7168, BF16
   * the GPU path (libfp8q wgrad: partial sums over 128 tokens, promoted to
     FP32 with the tile scales) -- measured, with the partials formed at
     float32 grade (default) and inside the FP8 matrix core (acc="fp8_mfma"),
-    next to the oracle's model of that unit; and, with power-of-two scales,
+    next to the hardware model of that unit (tests/fp8_unit_model.py); and, with power-of-two scales,
     the matrix core applying the scales and keeping the whole sum
     (acc="fp8_mfma_scaled", no promotion) next to the promoted forms;
   * emulated accumulators (oracle.accum): a float32 accumulator and a W-bit

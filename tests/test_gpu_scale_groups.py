@@ -11,8 +11,8 @@ row, block or group moves an output far outside the tolerance.
 
 Acceptance as in the other GEMM parity tests: the FP32-grade form within
 1e-5 * S + 1e-6 of the oracle on every element; the FP8-unit forms against
-the oracle's model of that unit (oracle.accum) with the allowances of
-tests/test_gpu_native.py, on a sample that covers every row and every column
+the hardware model of that unit (tests/fp8_unit_model.py, no parity claim)
+with the allowances of tests/test_gpu_native.py, on a sample that covers every row and every column
 (so every scale entry).
 """
 
