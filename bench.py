@@ -299,6 +299,11 @@ def moe(torch, fp8q, lib, clock, sp, reps):
     a_up, s_up = fp8q.gather_rows(xq, xs, gather)
     off = torch.from_numpy(d["offsets"]).to("cuda:0")
     hq, hs = fp8q.quantize_act(bf16_dev(torch, d["h"]))
+    # power-of-two operands for the fp32_pow2 form
+    xq2, xs2 = fp8q.quantize_act(x, scale_mode="pow2")
+    a_up2, s_up2 = fp8q.gather_rows(xq2, xs2, gather)
+    hq2, hs2 = fp8q.quantize_act(bf16_dev(torch, d["h"]), scale_mode="pow2")
+    del xq2, xs2
     out = {"experts": G, "rows_per_expert": [int(v) for v in d["counts"]], "rows": rows}
 
     nb_up = k_up // 128
@@ -331,10 +336,12 @@ def moe(torch, fp8q, lib, clock, sp, reps):
     del sxs, sx0, cq, cs
 
     weights = {}
-    for name, wname, in_a, in_s in (("up_7168x4096", "w_up", a_up, s_up), ("down_2048x7168", "w_down", hq, hs)):
+    for name, wname, in_a, in_s, in_a2, in_s2 in (("up_7168x4096", "w_up", a_up, s_up, a_up2, s_up2),
+                                                  ("down_2048x7168", "w_down", hq, hs, hq2, hs2)):
         wb = bf16_dev(torch, d[wname])
         g, n, k = wb.shape
         wq, wsc = fp8q.quantize_weight(wb.view(g * n, k))
+        wq2, wsc2 = fp8q.quantize_weight(wb.view(g * n, k), scale_mode="pow2")
         del wb
         weights[wname] = (wq, wsc, n, k)
         c = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda:0")
@@ -346,16 +353,20 @@ def moe(torch, fp8q, lib, clock, sp, reps):
                 per += max(2.0 * int(m) * n * k / (FP8_PEAK_TFLOPS * 1e6),
                            (n * k + (n // 128) * (k // 128) * 4 + int(m) * (k + (k // 128) * 4 + n * 2))
                            / (HBM_PEAK_GBS * 1e3))
-        for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
-            def fn(i, acc=acc, in_a=in_a, in_s=in_s, wq=wq, wsc=wsc, n=n, k=k, c=c):
-                return lib.fp8q_grouped_gemm_ex(in_a.data_ptr(), in_s.data_ptr(), off.data_ptr(), G, rows,
-                                                wq.data_ptr(), wsc.data_ptr(), n, k, fp8q.OUT_BF16, acc,
+        for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA),
+                              ("_fp32_pow2", fp8q.ACC_FP32_POW2)):
+            p2 = acc == fp8q.ACC_FP32_POW2
+            ops = (in_a2, in_s2, wq2, wsc2) if p2 else (in_a, in_s, wq, wsc)
+
+            def fn(i, acc=acc, ops=ops, n=n, k=k, c=c):
+                return lib.fp8q_grouped_gemm_ex(ops[0].data_ptr(), ops[1].data_ptr(), off.data_ptr(), G, rows,
+                                                ops[2].data_ptr(), ops[3].data_ptr(), n, k, fp8q.OUT_BF16, acc,
                                                 c.data_ptr(), n, sp)
             r = clock.stats(fn, reps, flop=flop, nbytes=nbytes)
             r.update(roofline_entry(flop, nbytes, r.get("batch_avg_us", r["median_us"])))
             r["per_expert_roofline_us"] = round(per, 2)
             out[name + acc_name] = r
-        del c
+        del c, wq2, wsc2
 
     wq_u, ws_u, n_u, k_u = weights["w_up"]
     wq_d, ws_d, n_d, k_d = weights["w_down"]
@@ -399,17 +410,19 @@ def wgrad(torch, fp8q, lib, clock, sp, reps):
         nbytes = tok * feat * 3 + feat * (tok // 128) * 4
         out[f"quantize_{name}_token_t_{tok}x{feat}"] = clock.stats(fn, reps, nbytes=nbytes)
         fn(0)
-        q[name] = (codes, scales, tok, feat)
+        q[name] = (codes, scales, tok, feat) + fp8q.quantize_act(t, tile_axis="token_t", scale_mode="pow2")
         del t, t2
-    dyc, dys, T, nout = q["dy"]
-    xc, xs, _, kin = q["x"]
+    dyc, dys, T, nout, dyc2, dys2 = q["dy"]
+    xc, xs, _, kin, xc2, xs2 = q["x"]
     dw = torch.empty((nout, kin), dtype=torch.float32, device="cuda:0")
     flop = 2.0 * nout * kin * T
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
-    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
-        def fg(i, acc=acc):
-            return lib.fp8q_wgrad_ex(dyc.data_ptr(), dys.data_ptr(), xc.data_ptr(), xs.data_ptr(), nout, kin, T, acc,
-                                     dw.data_ptr(), kin, sp)
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2)):
+        ops = (dyc2, dys2, xc2, xs2) if acc == fp8q.ACC_FP32_POW2 else (dyc, dys, xc, xs)
+
+        def fg(i, acc=acc, ops=ops):
+            return lib.fp8q_wgrad_ex(ops[0].data_ptr(), ops[1].data_ptr(), ops[2].data_ptr(), ops[3].data_ptr(), nout,
+                                     kin, T, acc, dw.data_ptr(), kin, sp)
         r = clock.stats(fg, reps, flop=flop, nbytes=nbytes)
         r.update(roofline_entry(flop, nbytes, r.get("batch_avg_us", r["median_us"])))
         out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = r
@@ -440,10 +453,16 @@ def dgrad(torch, fp8q, lib, clock, sp, reps, w):
     dx = torch.empty((m, k), dtype=torch.bfloat16, device="cuda:0")
     flop = 2.0 * m * n * k
     nbytes = m * n + n * k + m * (n // 128) * 4 + (k // 128) * (n // 128) * 4 + m * k * 2
-    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA)):
-        def fg(i, acc=acc):
-            return lib.fp8q_gemm_ex(dyq.data_ptr(), dys.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), m, k, n,
-                                    fp8q.OUT_BF16, acc, dx.data_ptr(), k, sp)
+    # the same operands with power-of-two scales, for the fp32_pow2 form
+    dyq2, dys2 = fp8q.quantize_act(dy, scale_mode="pow2")
+    _, _, ct2, st2 = fp8q.quantize_weight_t(w, scale_mode="pow2", both=False)
+    ct2 = ct2.contiguous()
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2)):
+        ops = (dyq2, dys2, ct2, st2) if acc == fp8q.ACC_FP32_POW2 else (dyq, dys, codes_t, scales_t)
+
+        def fg(i, acc=acc, ops=ops):
+            return lib.fp8q_gemm_ex(ops[0].data_ptr(), ops[1].data_ptr(), ops[2].data_ptr(), ops[3].data_ptr(), m, k,
+                                    n, fp8q.OUT_BF16, acc, dx.data_ptr(), k, sp)
         r = clock.stats(fg, reps, flop=flop, nbytes=nbytes)
         r.update(roofline_entry(flop, nbytes, r.get("batch_avg_us", r["median_us"])))
         out[f"dgrad_{m}x{k}x{n}{acc_name}"] = r
@@ -725,6 +744,12 @@ def main():
     dense["gemm_block_scaled_fp8_mfma_scaled_pow2"] = clock.stats(
         lambda i: lib.fp8q_gemm_ex(ap_c.data_ptr(), ap_s.data_ptr(), wp_c.data_ptr(), wp_s.data_ptr(), M, N, K,
                                    fp8q.OUT_BF16, fp8q.ACC_FP8_MFMA_SCALED, c.data_ptr(), N, sp), reps, flop=GEMM_FLOP)
+    # float32 grade with power-of-two scales applied while widening (no fold)
+    dense["gemm_block_scaled_fp32_pow2"] = clock.stats(
+        lambda i: lib.fp8q_gemm_ex(ap_c.data_ptr(), ap_s.data_ptr(), wp_c.data_ptr(), wp_s.data_ptr(), M, N, K,
+                                   fp8q.OUT_BF16, fp8q.ACC_FP32_POW2, c.data_ptr(), N, sp), reps, flop=GEMM_FLOP)
+    dense["gemm_block_scaled_fp32_pow2"]["frac_bf16_peak"] = round(
+        GEMM_FLOP / dense["gemm_block_scaled_fp32_pow2"]["batch_avg_us"] / 1e6 / BF16_PEAK_TFLOPS, 4)
     del ap_c, ap_s, wp_c, wp_s
     clock.release()
 

@@ -138,7 +138,8 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, int
 namespace {
 // GEMM kernels address an operand with 32-bit byte offsets.
 bool acc_ok(int acc) {
-  return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA || acc == FP8Q_ACC_FP8_MFMA_SCALED;
+  return acc == FP8Q_ACC_FP32 || acc == FP8Q_ACC_FP8_MFMA || acc == FP8Q_ACC_FP8_MFMA_SCALED ||
+         acc == FP8Q_ACC_FP32_POW2;
 }
 
 constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;

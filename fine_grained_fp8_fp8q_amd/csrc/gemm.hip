@@ -123,6 +123,17 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(int lo, int hi) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// The same with the operand's scale applied by the convert: for a power of
+// two 2^e each E4M3 value times 2^e is again a BF16 value (exact), as long as
+// it stays in BF16's normal range.
+__device__ __forceinline__ v8bf e4m3x8_to_bf16_scaled(int lo, int hi, float s) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)lo, s, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)lo, s, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, s, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)hi, s, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 struct Tile {
   int m0, mend;  // rows [m0, mend) of A / C
   int n0;
@@ -551,6 +562,78 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     for (int f = 0; f < 4; ++f) fold(JN - 1, f);
   };
 
+  // Float32-grade form for power-of-two scales: each fragment is widened
+  // with its operand's scale applied by the convert (exact, see
+  // e4m3x8_to_bf16_scaled), so every product is sa*sw*a*w and all K blocks
+  // chain onto the same matrix-core accumulator: no fold.  The scales of a
+  // block are read before its refill (as in the FP32-grade form); the
+  // dense and grouped W scale of a column is its 128-column block's, the
+  // weight gradient's its own (in the stage).
+  auto compute_bf16s = [&](const uint8_t* st, const float* SA, auto& refill_now, auto jn) {
+    constexpr int JN = decltype(jn)::value;  // 16-column W fragments per wave
+    constexpr int WC = 16 * JN;
+    if (!active) {
+      refill_now();
+      return;
+    }
+    using L = decltype(layout_of(jn));
+    const float* S = reinterpret_cast<const float*>(st + L::kS);
+    const int arow0 = wm * 64 + r16;
+    const int wrow0 = wn * WC + r16;
+    float sa[4], sw[JN];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sa[f] = SA[(arow0 + f * 16) * 4];
+#pragma unroll
+    for (int j = 0; j < JN; ++j) sw[j] = MODE == kWgrad ? S[wrow0 + j * 16] : SA[(BM + wrow0 + j * 16) * 4];
+    refill_now();
+    const int wsw = swz(wrow0);
+    const uint8_t* Wb = st + L::kW + wrow0 * 128;
+    const uint8_t* w_lo = Wb + 16 * (c0 ^ wsw);
+    const uint8_t* w_hi = Wb + 16 * ((c0 + 1) ^ wsw);
+    auto read_w_lo = [&](int j, v4i& lo) { lo = *reinterpret_cast<const v4i*>(w_lo + j * 2048); };
+    auto read_w_hi = [&](int j, v4i& hi) { hi = *reinterpret_cast<const v4i*>(w_hi + j * 2048); };
+    auto part = [](const v4i& lo, const v4i& hi, int q, float sc) {
+      const v4i& r = q < 2 ? lo : hi;
+      return e4m3x8_to_bf16_scaled(r[(q & 1) * 2], r[(q & 1) * 2 + 1], sc);
+    };
+    const int asw = swz(arow0);
+    v8bf af[4][4];
+    v4i alo[4], ahi[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint8_t* base = st + (arow0 + f * 16) * 128;
+      alo[f] = *reinterpret_cast<const v4i*>(base + 16 * (c0 ^ asw));
+      ahi[f] = *reinterpret_cast<const v4i*>(base + 16 * ((c0 + 1) ^ asw));
+    }
+    v4i w0lo, w0hi, wlo, whi;
+    v8bf bf[4];
+    read_w_lo(0, w0lo);
+    read_w_hi(0, w0hi);
+    read_w_lo(1, wlo);
+    read_w_hi(1, whi);
+#pragma unroll
+    for (int j = 0; j < JN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (j == 0) {
+          bf[q] = part(w0lo, w0hi, q, sw[0]);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) af[f][q] = part(alo[f], ahi[f], q, sa[f]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          acc[f][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[q], af[f][q], acc[f][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j < JN - 1) bf[q] = part(wlo, whi, q, sw[j + 1]);
+        if (q == 1 && j < JN - 2) read_w_lo(j + 2, wlo);
+        if (q == 3 && j < JN - 2) read_w_hi(j + 2, whi);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // FP8 matrix-core form: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile
   // and K block reads the E4M3 bytes straight from LDS (lane group g holds
   // bytes 32g..32g+31 of its row, the instruction's operand layout).  Its
@@ -701,7 +784,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
     // this block's scales in the scale buffer: A entry e at SA[4 e], W
     // entry e at SA[4 (BM + e)]
     const float* SA = reinterpret_cast<const float*>(scl + ((kb >> 2) & 1) * kSclHalf) + (kb & 3);
-    if constexpr (ACC == 2) {
+    if constexpr (ACC == 3) {
+      compute_bf16s(st, SA, refill_now, jn);
+    } else if constexpr (ACC == 2) {
       compute_f8s(st, SA, refill_now, jn);
     } else if constexpr (ACC == 1) {
       compute_f8(st, SA, refill_now, jn);
@@ -889,7 +974,9 @@ int tile_width(int tiles_m, int n) {
 
 template <int MODE, int OUT, int NARROW>
 void launch_acc_w(const GemmArgs& g, int grid, int acc, hipStream_t stream) {
-  if (acc == 2) {
+  if (acc == 3) {
+    hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 3, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);
+  } else if (acc == 2) {
     hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 2, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);
   } else if (acc == 1) {
     hipLaunchKernelGGL((gemm_bs_kernel<MODE, OUT, 1, NARROW>), dim3(grid), dim3(kThreads), 0, stream, g);

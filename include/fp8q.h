@@ -95,8 +95,19 @@ enum { FP8Q_OUT_F32 = 0, FP8Q_OUT_BF16 = 1 };
  *    in-group alignment of FP8Q_ACC_FP8_MFMA applies, and the running sum
  *    is added to at about float32 grade once per group of 8 products.
  *    A scale that is not a power of two is used as the power of two of its
- *    exponent (results are then wrong). */
-enum { FP8Q_ACC_FP32 = 0, FP8Q_ACC_FP8_MFMA = 1, FP8Q_ACC_FP8_MFMA_SCALED = 2 };
+ *    exponent (results are then wrong).
+ *  FP8Q_ACC_FP32_POW2: for power-of-two scales only (FP8Q_SCALE_POW2 on both
+ *    operands), float32 grade like FP8Q_ACC_FP32: each operand is widened to
+ *    BF16 with its scale applied by the convert (an E4M3 value times 2^e is
+ *    again a BF16 value), so every BF16 matrix-core product is
+ *    sa * sw * a * w exactly and all K blocks accumulate in the matrix
+ *    core's float32 accumulator (tmdrlife.com wr_id=13334 ¶3-¶4: MMA with
+ *    group scaling, integral power-of-two scales): no VALU fold.  Results
+ *    satisfy the FP8Q_ACC_FP32 bound while every scaled operand stays in
+ *    BF16's normal range (scales in [2^-100, 2^100] or zero, which power-of-
+ *    two quantization of BF16 values with max-abs >= 2^-92 gives); scales
+ *    that are not powers of two give wrong results. */
+enum { FP8Q_ACC_FP32 = 0, FP8Q_ACC_FP8_MFMA = 1, FP8Q_ACC_FP8_MFMA_SCALED = 2, FP8Q_ACC_FP32_POW2 = 3 };
 enum {
   FP8Q_TILE_ROW = 0,    /* 1x128 tiles along cols: codes [rows, ld_codes], scales [rows, ceil(cols/128)] */
   FP8Q_TILE_TOKEN_T = 1 /* 128x1 tiles along rows (the token axis), codes written transposed:

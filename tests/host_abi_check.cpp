@@ -275,7 +275,10 @@ void gemms() {
   EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 100, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_ERR_SHAPE, false);
   EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4, 4, 100, FP8Q_OUT_F32, FP8Q_ACC_FP32, c, 4, stream_tag()), FP8Q_ERR_SHAPE,
          false);
-  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4, 4, 128, FP8Q_OUT_F32, 3, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 4, 4, 128, FP8Q_OUT_F32, 4, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
+  EXPECT(fp8q_gemm_ex(a, sa, w, sw, 64, 32, 256, FP8Q_OUT_BF16, FP8Q_ACC_FP32_POW2, c, 32, stream_tag()), FP8Q_OK,
+         true);
+  CHECK(last_is("gemm", {64, 32, 256, 1, FP8Q_ACC_FP32_POW2, 32}, {a, sa, w, sw, c}));
   EXPECT(fp8q_gemm(a, sa, w, sw, 4, 4, 128, 2, c, 4, stream_tag()), FP8Q_ERR_INVALID_ARG, false);
   // an operand of 2 GiB or more (32-bit byte offsets in the kernels)
   EXPECT(fp8q_gemm(a, sa, w, sw, 1 << 24, 4, 128, FP8Q_OUT_F32, c, 4, stream_tag()), FP8Q_ERR_SHAPE, false);

@@ -89,7 +89,7 @@ def test_gemm_validation(lib):
     gx = lib.fp8q_gemm_ex
     assert gx(None, None, None, None, 0, 4, 128, 0, 0, None, 4, None) == fp8q.OK
     assert gx(P16, P16, P16, P16, 4, 4, 100, 0, 1, P16, 4, None) == fp8q.ERR_SHAPE
-    assert gx(P16, P16, P16, P16, 4, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert gx(P16, P16, P16, P16, 4, 4, 128, 0, 4, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
     assert gx(P16, P16, P16, P16, 4, 4, 128, 0, -1, P16, 4, None) == fp8q.ERR_INVALID_ARG
 
 
@@ -134,7 +134,7 @@ def test_grouped_and_wgrad_validation(lib):
     assert gg(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, P16, 4, None) == fp8q.ERR_SHAPE
     assert gg(P16, P16, P8, 2, 10, P16, P16, 4, 128, 0, P16, 4, None) == fp8q.ERR_ALIGN
     ggx = lib.fp8q_grouped_gemm_ex
-    assert ggx(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 3, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert ggx(P16, P16, P16, 2, 10, P16, P16, 4, 128, 0, 4, P16, 4, None) == fp8q.ERR_INVALID_ARG  # acc
     assert ggx(P16, P16, P16, 2, 10, P16, P16, 4, 64, 0, 1, P16, 4, None) == fp8q.ERR_SHAPE
     wg = lib.fp8q_wgrad
     assert wg(P16, P16, P16, P16, 0, 4, 128, P16, 4, None) == fp8q.OK
@@ -167,7 +167,7 @@ def test_gemm_quantized_validation(lib):
     f = lib.fp8q_gemm_quantized
     # (a, sa, w, sw, M, N, K, acc, scale_mode, codes, ld_c, scales, stream)
     assert f(P16, P16, P16, P16, 0, 4, 128, 0, 0, None, 4, None, None) == fp8q.OK
-    assert f(P16, P16, P16, P16, 4, 4, 128, 3, 0, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG  # acc
+    assert f(P16, P16, P16, P16, 4, 4, 128, 4, 0, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG  # acc
     assert f(P16, P16, P16, P16, 4, 4, 128, 0, 2, P16, 4, P16, None) == fp8q.ERR_INVALID_ARG  # mode
     assert f(P16, P16, P16, P16, 4, 4, 128, 0, 0, P16, 4, None, None) == fp8q.ERR_INVALID_ARG  # scales
     assert f(P16, P16, P16, P16, 4, 4, 100, 0, 0, P16, 4, P16, None) == fp8q.ERR_SHAPE  # K % 128

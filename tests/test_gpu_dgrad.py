@@ -110,3 +110,18 @@ def test_dgrad_up_projection_sampled():
                 s = s + (2.0 ** -19) * t / 1e-5
             ok = G.accept_bf16(dx[r, q], ref, s)
             assert ok.all(), f"dgrad {acc} chunk {lo}: {int((~ok).sum())} bad"
+        if acc == "fp32":
+            # every element of whole output tiles: at this shape the launch
+            # uses tiles of 256 x 224 (512 of them fill the 256 CUs in two
+            # rounds), whose waves' 112 columns start inside a 128-column
+            # weight-scale block (tile 1: columns 224..447) or end the
+            # matrix (tile 31: columns 6944..7167)
+            for tm, tn in [(0, 1), (7, 10), (15, 31)]:
+                r0, c0 = 256 * tm, 224 * tn
+                # the oracle over the 128-aligned columns around the tile
+                # (weight-scale row b covers columns 128b..128b+127)
+                b0, b1 = c0 // 128, (c0 + 223) // 128 + 1
+                ref, s = G.gemm(dy_c[r0:r0 + 256], dy_s[r0:r0 + 256], wt_c[128 * b0:128 * b1], wt_s[b0:b1])
+                ref, s = ref[:, c0 - 128 * b0:c0 - 128 * b0 + 224], s[:, c0 - 128 * b0:c0 - 128 * b0 + 224]
+                ok = G.accept_bf16(dx[r0:r0 + 256, c0:c0 + 224], ref, s)
+                assert ok.all(), f"dgrad tile ({tm}, {tn}): {int((~ok).sum())} of {ok.size} bad"

@@ -9,7 +9,8 @@ gradient, with 1x128 tiles and 128x128 blocks whose magnitudes differ by up
 to 2^24 from block to block and row to row, so a scale taken from the wrong
 row, block or group moves an output far outside the tolerance.
 
-Acceptance as in the other GEMM parity tests: the FP32-grade form within
+Acceptance as in the other GEMM parity tests: the FP32-grade forms (and the
+power-of-two one, on operands quantized with power-of-two scales) within
 1e-5 * S + 1e-6 of the oracle on every element; the FP8-unit forms against
 the hardware model of that unit (tests/fp8_unit_model.py, no parity claim)
 with the allowances of tests/test_gpu_native.py, on a sample that covers every row and every column
@@ -62,16 +63,16 @@ def _block_spread(rng, n, k):
 
 
 @pytest.mark.parametrize("nkb", [6, 7, 9, 13])
-@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp8_mfma_scaled"])
+@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp8_mfma_scaled", "fp32_pow2"])
 def test_dense_scale_groups(nkb, acc):
     m, n, k = 200, 260, 128 * nkb
     rng = np.random.default_rng(100 + nkb)
-    mode = Q.POW2 if acc == "fp8_mfma_scaled" else Q.FREE
+    mode = Q.POW2 if acc in ("fp8_mfma_scaled", "fp32_pow2") else Q.FREE
     a_c, a_s = Q.quantize_rows(_tile_spread(rng, m, k), mode)
     w_c, w_s = Q.quantize_blocks(_block_spread(rng, n, k), mode)
     say(f"[scale groups] dense {m}x{n}x{k} acc={acc}")
     c = fp8q.gemm(dev(a_c), dev(a_s), dev(w_c), dev(w_s), out_dtype=torch.float32, acc=acc)
-    if acc == "fp32":
+    if acc in ("fp32", "fp32_pow2"):
         ref, s = G.gemm(a_c, a_s, w_c, w_s)
         _accept(c, ref, s, f"dense k/128={nkb}")
         return
@@ -86,7 +87,7 @@ def test_dense_scale_groups(nkb, acc):
 
 
 @pytest.mark.parametrize("n", [256, 328])
-@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma"])
+@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp32_pow2"])
 def test_grouped_scale_groups(acc, n):
     # four experts of 0, 70, 300 and 129 rows (tiles of every wave layout),
     # N a multiple of the tile width or not (a last N tile of 72 columns,
@@ -96,12 +97,13 @@ def test_grouped_scale_groups(acc, n):
     offs[1:] = np.cumsum(counts)
     rows, k = int(offs[-1]), 128 * 7
     rng = np.random.default_rng(7 + n)
-    a_c, a_s = Q.quantize_rows(_tile_spread(rng, rows, k))
-    q = [Q.quantize_blocks(_block_spread(rng, n, k)) for _ in counts]
+    mode = Q.POW2 if acc == "fp32_pow2" else Q.FREE
+    a_c, a_s = Q.quantize_rows(_tile_spread(rng, rows, k), mode)
+    q = [Q.quantize_blocks(_block_spread(rng, n, k), mode) for _ in counts]
     wc, ws = np.stack([c for c, _ in q]), np.stack([s for _, s in q])
     say(f"[scale groups] grouped {counts.tolist()} N={n} K={k} acc={acc}")
     c = fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out_dtype=torch.float32, acc=acc)
-    if acc == "fp32":
+    if acc in ("fp32", "fp32_pow2"):
         ref, s = G.grouped_gemm(a_c, a_s, offs, wc, ws)
         _accept(c, ref, s, f"grouped k/128=7 N={n}")
         return
@@ -116,7 +118,7 @@ def test_grouped_scale_groups(acc, n):
 
 
 @pytest.mark.parametrize("nkb", [7, 9])
-@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma"])
+@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp32_pow2"])
 def test_wgrad_scale_groups(nkb, acc):
     t_tok, nout, kin = 128 * nkb, 200, 300
     rng = np.random.default_rng(200 + nkb)
@@ -125,11 +127,12 @@ def test_wgrad_scale_groups(nkb, acc):
     e_x = np.repeat(rng.integers(-12, 13, (nkb, kin)), 128, axis=0)
     dy = synth.bf16_rne((rng.standard_normal((t_tok, nout)) * np.exp2(e_dy)).astype(np.float32))
     x = synth.bf16_rne((rng.standard_normal((t_tok, kin)) * np.exp2(e_x)).astype(np.float32))
-    dy_c, dy_s = Q.quantize_token_t(dy)
-    x_c, x_s = Q.quantize_token_t(x)
+    mode = Q.POW2 if acc == "fp32_pow2" else Q.FREE
+    dy_c, dy_s = Q.quantize_token_t(dy, mode)
+    x_c, x_s = Q.quantize_token_t(x, mode)
     say(f"[scale groups] wgrad T={t_tok} {nout}x{kin} acc={acc}")
     dw = fp8q.wgrad(dev(dy_c), dev(dy_s), dev(x_c), dev(x_s), acc=acc)
-    if acc == "fp32":
+    if acc in ("fp32", "fp32_pow2"):
         ref, s = G.wgrad(dy_c, dy_s, x_c, x_s)
         _accept(dw, ref, s, f"wgrad k/128={nkb}")
         return
