@@ -4,7 +4,7 @@
 With power-of-two scales (tmdrlife.com wr_id=13334 ¶4) an E4M3 code times
 its scale is a BF16 value, so the kernels widen each operand fragment with
 its scale already applied and accumulate every K block in the BF16 matrix
-core's float32 accumulator (the pages' "MMA with group scaling",
+core's float32 accumulator (the pages' group-scaled matrix multiply,
 tmdrlife.com wr_id=13334 ¶3), with no fold.  The bar is the same as for the
 default form: |gpu - oracle| <= 1e-5 * S + 1e-6 per element (BF16 output:
 the interval rule), on operands the oracle quantized with power-of-two
