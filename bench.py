@@ -212,6 +212,30 @@ def roofline_entry(flop, nbytes, med_us):
 
 # -------------------------------------------------------- workloads ----
 
+def plain_stream(torch, clock, sp, n_elems, reps, rot):
+    """The rate of a bare stream with a quantizer's traffic: the same number
+    of elements through libfp8q_streamref.so's 2:1 kernel (2 B read, 1 B
+    written per element, no arithmetic), over `rot` buffer sets like the
+    quantizer it stands next to."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fine_grained_fp8_fp8q_amd", "libfp8q_streamref.so"))
+    lib.fp8q_streamref_2to1.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.fp8q_streamref_2to1.restype = ctypes.c_int
+    n = (n_elems + 15) // 16 * 16
+    xs = [torch.empty(2 * n, dtype=torch.uint8, device="cuda:0") for _ in range(rot)]
+    ys = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(rot)]
+    r = clock.stats(lambda i: lib.fp8q_streamref_2to1(xs[i % rot].data_ptr(), ys[i % rot].data_ptr(), n, sp),
+                    reps, nbytes=3 * n)
+    return {"elements": n, "batch_avg_us": r["batch_avg_us"], "frac_hbm": r["frac_hbm"]}
+
+
+def with_stream(r, ps):
+    """Attach the same-size bare stream to a quantizer's entry."""
+    r["plain_stream_same_elements"] = ps
+    r["frac_of_plain_stream"] = round(ps["batch_avg_us"] / r["batch_avg_us"], 3)
+    return r
+
+
 def bf16_dev(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
@@ -264,6 +288,9 @@ def quantize_only(torch, fp8q, lib, clock, sp, reps):
         r["median_us_first_20_after_idle"] = round(clock.after_idle(fn), 2)
         out[f"act_16384x7168_{mode_name}"] = r
     del xs, cs, ss
+    ps = plain_stream(torch, clock, sp, rows * cols, reps, 2)
+    for mode_name in ("free", "pow2"):
+        with_stream(out[f"act_16384x7168_{mode_name}"], ps)
     wt = synth.quant_only_weight()
     n, k = wt.shape
     ws = [bf16_dev(torch, wt)]
@@ -278,6 +305,8 @@ def quantize_only(torch, fp8q, lib, clock, sp, reps):
     r = clock.stats(fw, reps, nbytes=wbytes)
     r["median_us_first_20_after_idle"] = round(clock.after_idle(fw), 2)
     out["weight_7168x18432"] = r
+    del ws, cs, ss
+    with_stream(r, plain_stream(torch, clock, sp, n * k, reps, 2))
     return out
 
 
@@ -408,7 +437,8 @@ def wgrad(torch, fp8q, lib, clock, sp, reps):
             return lib.fp8q_quantize_act(ts[i & 1].data_ptr(), tok, feat, feat, fp8q.TILE_TOKEN_T, fp8q.SCALE_FREE,
                                          codes.data_ptr(), tok, scales.data_ptr(), sp)
         nbytes = tok * feat * 3 + feat * (tok // 128) * 4
-        out[f"quantize_{name}_token_t_{tok}x{feat}"] = clock.stats(fn, reps, nbytes=nbytes)
+        out[f"quantize_{name}_token_t_{tok}x{feat}"] = with_stream(
+            clock.stats(fn, reps, nbytes=nbytes), plain_stream(torch, clock, sp, tok * feat, reps, 2))
         fn(0)
         q[name] = (codes, scales, tok, feat) + fp8q.quantize_act(t, tile_axis="token_t", scale_mode="pow2")
         del t, t2
@@ -699,6 +729,10 @@ def main():
     dense = {"quantize_act_1x128": clock.stats(q_act_i, reps, nbytes=ACT_BYTES),
              "quantize_weight_128x128": clock.stats(q_wgt_i, reps, nbytes=WGT_BYTES),
              "quantize_linear_act_and_weight": clock.stats(q_lin_i, reps, nbytes=ACT_BYTES + WGT_BYTES)}
+    ps = plain_stream(torch, clock, sp, M * K, reps, ROT)
+    with_stream(dense["quantize_act_1x128"], ps)
+    with_stream(dense["quantize_weight_128x128"], ps)
+    with_stream(dense["quantize_linear_act_and_weight"], plain_stream(torch, clock, sp, M * K + N * K, reps, ROT))
     dense["quantize_linear_after_cache_flush"] = clock.stats(lambda i: q_lin_i(0), 20, nbytes=ACT_BYTES + WGT_BYTES,
                                                              flush=True)
     del a_rot, w_rot, ac_rot, wc_rot

@@ -1,4 +1,5 @@
-"""Builds libfp8q.so (gfx950 only) in place with hipcc.
+"""Builds libfp8q.so (gfx950 only) in place with hipcc, and the bench's
+streaming reference libfp8q_streamref.so.
 
     python -m fine_grained_fp8_fp8q_amd.build
 
@@ -17,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
+# the bench's plain streaming kernel (a measuring stick, not part of libfp8q)
+STREAMREF_LIB = os.path.join(PKG, "libfp8q_streamref.so")
 
 SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_api.cpp"]
 
@@ -65,6 +68,9 @@ def build(verbose=False):
     # emit shows up here instead of when the library is loaded
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    tmp = STREAMREF_LIB + ".tmp"
+    _run([cc, *COMMON, "-shared", "-Wl,--no-undefined", os.path.join(CSRC, "stream_ref.hip"), "-o", tmp], verbose)
+    os.replace(tmp, STREAMREF_LIB)
     return LIB
 
 

@@ -345,12 +345,19 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
 // by 8 words per group of 8 features: the 64 lanes that write one word each
 // (8 feature groups x 8 token words) then hit 64 distinct banks, where the
 // unrotated rows put every feature group on the same two bank offsets.
+// rot4: the feature group turns with the token block inside aligned groups of
+// four feature groups.  With rows 4 KB apart (2048 features) the ~256
+// workgroups resident on an XCD otherwise read only about two distinct
+// 128-byte column offsets of every row; spreading them over four measured
+// 22.5 -> 21.3 us at 16384 x 2048 on MI355X.  The launcher sets it only when
+// every XCD's range of blocks holds whole groups, so each feature's scale
+// line is still written from one L2.
 template <bool POW2>
 __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __restrict__ x, int rows,
                                                             int cols, int64_t ldx,
                                                             uint8_t* __restrict__ codes, int64_t ldc,
                                                             float* __restrict__ scales, int ntb,
-                                                            bool vec) {
+                                                            bool vec, bool rot4) {
   constexpr int kRowBytes = 144;  // 16-byte aligned rows for the store reads
   __shared__ uint32_t red[4][64];
   // per-feature scale state, read back 8 features (32 bytes) at a time
@@ -369,7 +376,9 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
   const int logical = xcd_block(blockIdx.x, gridDim.x);
   const int tb = logical % ntb;
   const int t0 = tb * 128;
-  const int f0 = (logical / ntb) * 64;
+  int fg = logical / ntb;
+  if (rot4) fg = (fg & ~3) | ((fg + tb) & 3);
+  const int f0 = fg * 64;
   const bool full = vec && (t0 + 128 <= rows) && (f0 + 64 <= cols);
 
   uint4 v[4];
@@ -588,12 +597,18 @@ hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, b
 hipError_t launch_quant_token_t(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
                                 uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
   const int ntb = (rows + 127) / 128;
-  const dim3 grid(ntb * ((cols + 63) / 64)), block(256);
+  const int nblk = ntb * ((cols + 63) / 64);
+  const dim3 grid(nblk), block(256);
   const bool vec = ldx % 8 == 0 && ldc % 16 == 0;  // 16-byte loads and stores
+  // every XCD's contiguous range of blocks (xcd_block) is whole groups of
+  // four feature groups: rotation stays inside one XCD
+  const bool rot4 = nblk % 8 == 0 && (nblk / 8) % (4 * ntb) == 0;
   if (pow2) {
-    hipLaunchKernelGGL(quant_token_t_kernel<true>, grid, block, 0, stream, x, rows, cols, ldx, codes, ldc, scales, ntb, vec);
+    hipLaunchKernelGGL(quant_token_t_kernel<true>, grid, block, 0, stream, x, rows, cols, ldx, codes, ldc, scales, ntb, vec,
+                       rot4);
   } else {
-    hipLaunchKernelGGL(quant_token_t_kernel<false>, grid, block, 0, stream, x, rows, cols, ldx, codes, ldc, scales, ntb, vec);
+    hipLaunchKernelGGL(quant_token_t_kernel<false>, grid, block, 0, stream, x, rows, cols, ldx, codes, ldc, scales, ntb, vec,
+                       rot4);
   }
   return hipGetLastError();
 }

@@ -63,9 +63,12 @@ def test_ragged_rows(rows, cols, mode):
 
 
 # (700, 900) and (1500, 130): 6 x 15 and 12 x 3 workgroups, counts that the
-# eight XCDs do not divide, so the block order's uneven ranges are covered
+# eight XCDs do not divide, so the block order's uneven ranges are covered;
+# (300, 2040) and (1000, 4096): every XCD's range is whole groups of four
+# feature groups, so the launch rotates feature groups inside each group
+# (with a ragged last token block, and a ragged last feature group)
 @pytest.mark.parametrize("rows,cols", [(1, 1), (128, 64), (300, 70), (129, 200), (512, 128), (256, 1000),
-                                       (700, 900), (1500, 130)])
+                                       (700, 900), (1500, 130), (300, 2040), (1000, 4096)])
 @pytest.mark.parametrize("mode", ["free", "pow2"])
 def test_ragged_token_axis(rows, cols, mode):
     rng = np.random.default_rng(rows * 7 + cols)
