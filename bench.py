@@ -212,6 +212,12 @@ def roofline_entry(flop, nbytes, med_us):
 
 # -------------------------------------------------------- workloads ----
 
+def progress(msg):
+    """One line on stderr as each part of the run completes (the JSON line
+    alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def plain_stream(torch, clock, sp, n_elems, reps, rot):
     """The rate of a bare stream with a quantizer's traffic: the same number
     of elements through libfp8q_streamref.so's 2:1 kernel (2 B read, 1 B
@@ -787,11 +793,17 @@ def main():
     del ap_c, ap_s, wp_c, wp_s
     clock.release()
 
+    progress("config 2 (timed steps, quantizers, GEMM forms) done")
     configs = {"1_tiny_linear": tiny_linear(torch, fp8q, lib, clock, sp), "2_dense_up": dense}
+    progress("config 1 done")
     configs["dgrad_of_2"] = dgrad(torch, fp8q, lib, clock, sp, reps, w)
+    progress("Dgrad done")
     configs["3_quantize_only"] = quantize_only(torch, fp8q, lib, clock, sp, reps)
+    progress("config 3 done")
     configs["4_moe_grouped"] = moe(torch, fp8q, lib, clock, sp, reps)
+    progress("config 4 done")
     configs["5_wgrad"] = wgrad(torch, fp8q, lib, clock, sp, reps)
+    progress("config 5 done")
 
     traffic = GEMM_TRAFFIC["bytes"] if GEMM_TRAFFIC["source_sha256"] == source_sha256("gemm.hip") else None
     achieved = GEMM_FLOP / gemm_live_us / 1e6
@@ -837,6 +849,7 @@ def main():
     }
     out["rocm_smi_clocks_after_run"] = rocm_smi_clocks()
     if not args.no_cpu_baseline:
+        progress("timing the oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(step_outputs)
     print(json.dumps(out), flush=True)
 
