@@ -61,9 +61,9 @@ GEMM_MIN_BYTES = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 
 # when csrc/gemm.hip no longer hashes to `source_sha256` the bench reports
 # traffic null.
 GEMM_TRAFFIC = {"bytes": 216190000,
-                "source_sha256": "4566ded5c71afc190704053eadb13a4b350818d4a5c3a2a12f6a2bea0ac3bf10",
-                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,416.7 KiB x 2.000 "
-                           "+ WRITE_SIZE 34,305.4 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
+                "source_sha256": "a19cc29ec6707f5cb26530d1b19464ab9a58461561f37cec286ec4e3eddf38db",
+                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,414.8 KiB x 2.000 "
+                           "+ WRITE_SIZE 34,305.7 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
 
 
 def parse():
