@@ -453,8 +453,10 @@ def wgrad(torch, fp8q, lib, clock, sp, reps):
     dw = torch.empty((nout, kin), dtype=torch.float32, device="cuda:0")
     flop = 2.0 * nout * kin * T
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
-    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2)):
-        ops = (dyc2, dys2, xc2, xs2) if acc == fp8q.ACC_FP32_POW2 else (dyc, dys, xc, xs)
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2),
+                          ("_fp8_mfma_scaled_pow2", fp8q.ACC_FP8_MFMA_SCALED)):
+        p2 = acc in (fp8q.ACC_FP32_POW2, fp8q.ACC_FP8_MFMA_SCALED)
+        ops = (dyc2, dys2, xc2, xs2) if p2 else (dyc, dys, xc, xs)
 
         def fg(i, acc=acc, ops=ops):
             return lib.fp8q_wgrad_ex(ops[0].data_ptr(), ops[1].data_ptr(), ops[2].data_ptr(), ops[3].data_ptr(), nout,
@@ -493,8 +495,10 @@ def dgrad(torch, fp8q, lib, clock, sp, reps, w):
     dyq2, dys2 = fp8q.quantize_act(dy, scale_mode="pow2")
     _, _, ct2, st2 = fp8q.quantize_weight_t(w, scale_mode="pow2", both=False)
     ct2 = ct2.contiguous()
-    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2)):
-        ops = (dyq2, dys2, ct2, st2) if acc == fp8q.ACC_FP32_POW2 else (dyq, dys, codes_t, scales_t)
+    for acc_name, acc in (("", fp8q.ACC_FP32), ("_fp8_mfma", fp8q.ACC_FP8_MFMA), ("_fp32_pow2", fp8q.ACC_FP32_POW2),
+                          ("_fp8_mfma_scaled_pow2", fp8q.ACC_FP8_MFMA_SCALED)):
+        p2 = acc in (fp8q.ACC_FP32_POW2, fp8q.ACC_FP8_MFMA_SCALED)
+        ops = (dyq2, dys2, ct2, st2) if p2 else (dyq, dys, codes_t, scales_t)
 
         def fg(i, acc=acc, ops=ops):
             return lib.fp8q_gemm_ex(ops[0].data_ptr(), ops[1].data_ptr(), ops[2].data_ptr(), ops[3].data_ptr(), m, k,

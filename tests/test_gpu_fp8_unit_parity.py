@@ -13,6 +13,9 @@ forms meet the tolerance depends on the operands' spread inside a group:
 * the weight-gradient workload (dY 16384 x 2048, X 16384 x 7168, ~N(0,1),
   128-token tiles; free and power-of-two scales) meets it: asserted here on
   sampled outputs and on two whole 256 x 224 output tiles;
+* so does the activation gradient of the up-projection (dY 4096 x 4096
+  ~N(0,1) in 1x128 tiles times W 4096 x 7168 ~N(0,0.02)): asserted on
+  sampled outputs and on two whole 256 x 224 output tiles;
 * the workloads with outliers (tiny linear: 0.5% of A x50; dense
   up-projection and MoE: 0.1% x100) do not: their fractions within tolerance
   are measured and reported (printed, and written as JSON when
@@ -89,6 +92,42 @@ def test_fp8_unit_forms_meet_tolerance_on_wgrad(mode, acc):
     ok = G.accept_f32(got, ref, s)
     assert ok.all(), (f"wgrad {acc} ({mode}): {int((~ok).sum())} of {ok.size} outside 1e-5*S+1e-6; "
                       f"max err/S {float((np.abs(got - ref) / s).max()):.3g}")
+
+
+_DGRAD = {}
+
+
+@pytest.mark.parametrize("mode,acc", [("free", "fp8_mfma"), ("pow2", "fp8_mfma"), ("pow2", "fp8_mfma_scaled")])
+def test_fp8_unit_forms_meet_tolerance_on_dgrad(mode, acc):
+    """dX [4096, 7168] = dY [4096, 4096] . W over N = 4096, operands
+    quantized by the oracle (dY per 1x128 tile along N, W per 128x128
+    block and transposed), FP32 out."""
+    qm = Q.POW2 if mode == "pow2" else Q.FREE
+    if mode not in _DGRAD:
+        w = synth.dense_up()["w"]
+        dy = synth.bf16_rne(np.random.default_rng(21).standard_normal((4096, 4096)).astype(np.float32))
+        say(f"[fp8-unit] dgrad operands ({mode}, oracle quantization)")
+        dy_c, dy_s = Q.quantize_rows(dy, qm)
+        w_c, w_s = Q.quantize_blocks(w, qm)
+        _DGRAD[mode] = (dy_c, dy_s, np.ascontiguousarray(w_c.T), np.ascontiguousarray(w_s.T))
+    dy_c, dy_s, wt_c, wt_s = _DGRAD[mode]
+    say(f"[fp8-unit] dgrad 4096x7168 over 4096 acc={acc} scales={mode}")
+    dx = host(fp8q.gemm(dev(dy_c), dev(dy_s), dev(wt_c), dev(wt_s), out_dtype=torch.float32,
+                        acc=acc)).astype(np.float64)
+    rng = np.random.default_rng(23)
+    rows, cols = rng.integers(0, 4096, 4000), rng.integers(0, 7168, 4000)
+    ref, s = G.gemm_at(dy_c, dy_s, wt_c, wt_s, rows, cols)
+    ok = G.accept_f32(dx[rows, cols], ref, s)
+    assert ok.all(), f"dgrad {acc} ({mode}) sampled: {int((~ok).sum())} outside the tolerance"
+    for tm, tn in [(0, 1), (15, 31)]:
+        r0, c0 = 256 * tm, 224 * tn
+        b0, b1 = c0 // 128, (c0 + 223) // 128 + 1
+        ref, s = G.gemm(dy_c[r0:r0 + 256], dy_s[r0:r0 + 256], wt_c[128 * b0:128 * b1], wt_s[b0:b1])
+        ref, s = ref[:, c0 - 128 * b0:c0 - 128 * b0 + 224], s[:, c0 - 128 * b0:c0 - 128 * b0 + 224]
+        got = dx[r0:r0 + 256, c0:c0 + 224]
+        ok = G.accept_f32(got, ref, s)
+        assert ok.all(), (f"dgrad {acc} ({mode}) tile ({tm}, {tn}): {int((~ok).sum())} of {ok.size} outside; "
+                          f"max err/S {float((np.abs(got - ref) / s).max()):.3g}")
 
 
 def _fraction(got, ref, s, bf16):
