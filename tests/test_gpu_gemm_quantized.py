@@ -58,6 +58,24 @@ def test_small_every_tile(m, n, k, mode):
     assert bad.size == 0, f"{len(bad)} of {ok.size} tiles rejected, first {tuple(bad[0])}"
 
 
+@pytest.mark.parametrize("m,n,k", [(70, 256, 384), (300, 384, 512), (64, 520, 1024)])
+@pytest.mark.parametrize("mode", ["free", "pow2"])
+def test_small_every_tile_fp32_pow2(m, n, k, mode):
+    """The float32-grade form for power-of-two operand scales writing the
+    quantized output (output tiles in either scale mode)."""
+    rng = np.random.default_rng(m * 17 + n * 5 + k)
+    qm = Q.POW2 if mode == "pow2" else Q.FREE
+    a = synth.bf16_rne(rng.standard_normal((m, k)).astype(np.float32))
+    w = synth.bf16_rne((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    ac, as_ = Q.quantize_rows(a, Q.POW2)
+    wc, ws = Q.quantize_blocks(w, Q.POW2)
+    say(f"[gemm-q] {m}x{n}x{k} out {mode}, acc fp32_pow2")
+    codes, scales = fp8q.gemm_quantized(dev(ac), dev(as_), dev(wc), dev(ws), scale_mode=mode, acc="fp32_pow2")
+    c, s = G.gemm(ac, as_, wc, ws)
+    ok = G.accept_quantized(host_codes(codes), host(scales), c, s, qm)
+    assert ok.all(), f"{int((~ok).sum())} of {ok.size} tiles rejected"
+
+
 @pytest.mark.parametrize("mode", ["free", "pow2"])
 def test_dense_up_projection_sampled_rows(mode):
     d = synth.dense_up()
@@ -76,11 +94,11 @@ def test_dense_up_projection_sampled_rows(mode):
     assert ok.all(), f"{int((~ok).sum())} of {ok.size} tiles rejected"
 
 
-@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp8_mfma_scaled"])
+@pytest.mark.parametrize("acc", ["fp32", "fp8_mfma", "fp8_mfma_scaled", "fp32_pow2"])
 def test_fused_equals_gemm_then_quantize(acc):
     rng = np.random.default_rng(3)
     for m, n, k in ((4096, 4096, 7168), (333, 520, 256)):
-        mode = Q.POW2 if acc == "fp8_mfma_scaled" else Q.FREE
+        mode = Q.POW2 if acc in ("fp8_mfma_scaled", "fp32_pow2") else Q.FREE
         if (m, n, k) == (4096, 4096, 7168) and mode == Q.FREE:
             d = synth.dense_up()
             a, w = dev_bf16(d["a"]), dev_bf16(d["w"])
