@@ -9,7 +9,9 @@ dW = dY^T X over 16384 tokens (dY 16384 x 2048, X 16384 x 7168, BF16
     float32 grade (default) and inside the FP8 matrix core (acc="fp8_mfma"),
     next to the hardware model of that unit (tests/fp8_unit_model.py); and, with power-of-two scales,
     the matrix core applying the scales and keeping the whole sum
-    (acc="fp8_mfma_scaled", no promotion) next to the promoted forms;
+    (acc="fp8_mfma_scaled", no promotion) and the BF16 matrix core
+    keeping the whole sum in float32 with the scales applied exactly in the
+    operands (acc="fp32_pow2", no promotion) next to the promoted forms;
   * emulated accumulators (oracle.accum): a float32 accumulator and a W-bit
     fixed-point accumulator aligned to the running maximum exponent, each
     with promotion every 128 products and with no promotion at all (one
@@ -106,7 +108,8 @@ def test_promotion_study():
     assert_codes_equal(host_codes(xq2)[csel], xc2, "X codes (pow2)")
     exact2, s2 = G.gemm_at(dyc2, dysc2, xc2, xsc2, ri, ci, w_block_rows=False)
     for name, acc in (("fp32_interval_128", "fp32"), ("fp8_mfma_interval_128", "fp8_mfma"),
-                      ("fp8_mfma_scaled_no_promotion", "fp8_mfma_scaled")):
+                      ("fp8_mfma_scaled_no_promotion", "fp8_mfma_scaled"),
+                      ("fp32_grade_no_promotion", "fp32_pow2")):
         got = host(fp8q.wgrad(dyq2, dys2, xq2, xs2, acc=acc)).astype(np.float64)
         report[f"pow2_gpu_{name}"] = _stats(got[rows, cols], exact2, s2)
 
@@ -119,6 +122,9 @@ def test_promotion_study():
     assert report["gpu_interval_128"]["within_tolerance"] == 1.0
     assert report["emulated_fp32_interval_128"]["within_tolerance"] == 1.0
     assert report["pow2_gpu_fp32_interval_128"]["within_tolerance"] == 1.0
+    # float32 accumulation of the whole sum, scales applied exactly in the
+    # operands (no promotion step): float32 grade too
+    assert report["pow2_gpu_fp32_grade_no_promotion"]["within_tolerance"] == 1.0
     # promotion is what keeps a narrow accumulator usable: at every width the
     # promoted sum is more accurate than the unpromoted one
     for w in WIDTHS:
