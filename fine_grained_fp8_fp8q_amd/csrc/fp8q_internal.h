@@ -9,14 +9,15 @@ namespace fp8q {
 
 // Grid sizes of the streaming kernels (host code; 64-bit arithmetic, so a
 // tile count up to 2^31 - 1 cannot overflow here).
-//  rows_grid: the 1x128 row quantizer, one pass per wave (64 tiles per
-//    256-thread workgroup) up to kMaxRowsGrid workgroups, then a grid-stride
-//    loop whose stride is 64 * kMaxRowsGrid tiles.
+//  rows_grid: the 1x128 row quantizer, one pass per wave (16 tiles per
+//    wave: 64 per 256-thread workgroup, 16 per 64-thread workgroup) up to
+//    kMaxRowsGrid workgroups, then a grid-stride loop whose stride is
+//    tiles_per_wg * kMaxRowsGrid tiles.
 //  stream_grid: four waves per workgroup, up to kMaxStreamGrid workgroups.
 constexpr int kMaxRowsGrid = 1 << 20;
 constexpr int kMaxStreamGrid = 2048;
-inline int rows_grid(int64_t ntiles) {
-  const int64_t want = (ntiles + 63) / 64;
+inline int rows_grid(int64_t ntiles, int tiles_per_wg = 64) {
+  const int64_t want = (ntiles + tiles_per_wg - 1) / tiles_per_wg;
   return (int)(want < kMaxRowsGrid ? want : kMaxRowsGrid);
 }
 inline int stream_grid(int64_t waves_needed) {

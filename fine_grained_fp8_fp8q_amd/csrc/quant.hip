@@ -51,9 +51,10 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
   const int grp = lane >> 4;
   const int sub = lane & 15;
   // Tile indices count in 32-bit unsigned: ntiles < 2^31 and the stride is
-  // at most 16 * 4 * kMaxRowsGrid = 2^26, so base + stride never wraps.
-  const uint32_t wave = ((uint32_t)bid * 256u + threadIdx.x) >> 6;
-  const uint32_t step = (uint32_t)nblocks * 64u;
+  // at most 16 tiles x 4 waves x kMaxRowsGrid = 2^26, so base + stride never
+  // wraps.  (Workgroups of 64 or 256 threads: 16 tiles per wave.)
+  const uint32_t wave = ((uint32_t)bid * blockDim.x + threadIdx.x) >> 6;
+  const uint32_t step = (uint32_t)nblocks * (blockDim.x >> 2);
 
   for (uint32_t base = wave * 16u; base < (uint32_t)ntiles; base += step) {
     uint4 v[4];
@@ -523,16 +524,20 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------ launchers ---
-// rows_grid (fp8q_internal.h): one pass per wave (64 tiles per 256-thread
-// workgroup) up to 2^20 workgroups; a large grid keeps more loads in flight
-// than a grid-stride loop over a capped grid (measured on MI355X: 4.7 TB/s at
-// 2048 workgroups vs 5.8 TB/s with one pass for this 2:1 read:write stream).
+// rows_grid (fp8q_internal.h): one pass per wave (16 tiles per wave) up to
+// 2^20 workgroups; a large grid keeps more loads in flight than a
+// grid-stride loop over a capped grid (measured on MI355X: 4.7 TB/s at 2048
+// workgroups vs 5.8 TB/s with one pass for this 2:1 read:write stream).  The
+// row quantizer launches one-wave workgroups: 16.5 -> 16.0 us at 4096 x 7168
+// and 6.0 -> 5.75 us at 3773 x 2048 against four-wave ones (no change at
+// 16384 x 7168); the combined linear launch keeps four waves, which its
+// weight blocks need.
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
                              uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
   const int nb = (cols + 127) / 128;
   const int ntiles = rows * nb;
-  const dim3 grid(rows_grid(ntiles)), block(256);
+  const dim3 grid(rows_grid(ntiles, 16)), block(64);
   const bool vec = ldx % 8 == 0 && ldc % 8 == 0;  // 16-byte loads, 8-byte stores
   if (pow2) {
     hipLaunchKernelGGL(quant_rows_kernel<true>, grid, block, 0, stream, x, cols, ldx, codes, ldc, scales, nb, ntiles, vec);

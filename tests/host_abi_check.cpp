@@ -382,11 +382,13 @@ void large_sweeps() {
                            stream_tag()),
          FP8Q_ERR_SHAPE, false);
   for (int64_t ntiles : {int64_t(1), int64_t(63), int64_t(64), int64_t(1) << 26, rows, (int64_t(1) << 31) - 1}) {
-    const int g = fp8q::rows_grid(ntiles);
-    CHECK(g >= 1 && g <= fp8q::kMaxRowsGrid);
-    CHECK(int64_t(g) * 64 >= std::min<int64_t>(ntiles, int64_t(fp8q::kMaxRowsGrid) * 64));
-    const uint64_t stride = uint64_t(g) * 64;  // tiles per sweep of the whole grid
-    CHECK(uint64_t(ntiles - 1) + stride < (uint64_t(1) << 32));
+    for (int per_wg : {16, 64}) {  // one-wave and four-wave workgroups
+      const int g = fp8q::rows_grid(ntiles, per_wg);
+      CHECK(g >= 1 && g <= fp8q::kMaxRowsGrid);
+      CHECK(int64_t(g) * per_wg >= std::min<int64_t>(ntiles, int64_t(fp8q::kMaxRowsGrid) * per_wg));
+      const uint64_t stride = uint64_t(g) * per_wg;  // tiles per sweep of the whole grid
+      CHECK(uint64_t(ntiles - 1) + stride < (uint64_t(1) << 32));
+    }
     const int sg = fp8q::stream_grid((ntiles + 3) / 4);
     CHECK(sg >= 1 && sg <= fp8q::kMaxStreamGrid);
     CHECK(uint64_t(ntiles - 1) + uint64_t(sg) * 16 < (uint64_t(1) << 32));
