@@ -10,7 +10,7 @@ namespace fp8q {
 // Grid sizes of the streaming kernels (host code; 64-bit arithmetic, so a
 // tile count up to 2^31 - 1 cannot overflow here).
 //  rows_grid: the 1x128 row quantizer, one pass per wave (16 tiles per
-//    wave: 64 per 256-thread workgroup, 16 per 64-thread workgroup) up to
+//    wave: 16 per 64-thread workgroup, 128 per 512-thread workgroup) up to
 //    kMaxRowsGrid workgroups, then a grid-stride loop whose stride is
 //    tiles_per_wg * kMaxRowsGrid tiles.
 //  stream_grid: four waves per workgroup, up to kMaxStreamGrid workgroups.

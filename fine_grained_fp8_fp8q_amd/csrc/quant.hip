@@ -51,8 +51,8 @@ __device__ __forceinline__ void quant_rows_body(int bid, int nblocks, const uint
   const int grp = lane >> 4;
   const int sub = lane & 15;
   // Tile indices count in 32-bit unsigned: ntiles < 2^31 and the stride is
-  // at most 16 tiles x 4 waves x kMaxRowsGrid = 2^26, so base + stride never
-  // wraps.  (Workgroups of 64 or 256 threads: 16 tiles per wave.)
+  // at most 16 tiles x 8 waves x kMaxRowsGrid = 2^27, so base + stride never
+  // wraps.  (Workgroups of 64 or 512 threads: 16 tiles per wave.)
   const uint32_t wave = ((uint32_t)bid * blockDim.x + threadIdx.x) >> 6;
   const uint32_t step = (uint32_t)nblocks * (blockDim.x >> 2);
 
@@ -136,14 +136,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 }
 
 // ------------------------------------------------------ 128x128 blocks ---
-// One workgroup (4 waves) per block.  Thread t holds rows t/16 + 16p
-// (p = 0..7) of the block, 8 BF16 each, so the block is read once and kept
-// in registers across the max-abs reduction.
+// One workgroup (8 waves) per block.  Thread t holds rows t/16 + 32p
+// (p = 0..3) of the block, 8 BF16 each, so the block is read once and kept
+// in registers across the max-abs reduction.  Eight waves of four rows each
+// measured faster than four waves of eight rows (7168 x 18432: 68.0 ->
+// 66.6 us; 4096 x 7168: 17.3 -> 17.1 us; 300 x 1000: 8.6 -> 7.4 us).
+constexpr int kBlockThreads = 512;
 template <bool POW2>
 __device__ __forceinline__ void quant_blocks_body(int bid, const uint16_t* __restrict__ w, int n, int k,
                                                   int64_t ldw, uint8_t* __restrict__ codes, int64_t ldc,
                                                   float* __restrict__ scales, int bk, bool vec) {
-  __shared__ uint32_t red[4];
+  constexpr int kWaves = kBlockThreads / 64, kRows = 128 / (kBlockThreads / 16);  // rows per thread
+  __shared__ uint32_t red[kWaves];
   const int tid = threadIdx.x;
   const int sub = tid & 15;
   const int r0 = tid >> 4;
@@ -152,10 +156,10 @@ __device__ __forceinline__ void quant_blocks_body(int bid, const uint16_t* __res
   const int row0 = bi * 128, col0 = bj * 128 + sub * 8;
   const bool full = vec && (row0 + 128 <= n) && (bj * 128 + 128 <= k);
 
-  uint4 v[8];
+  uint4 v[kRows];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int r = row0 + r0 + 16 * p;
+  for (int p = 0; p < kRows; ++p) {
+    const int r = row0 + r0 + (kBlockThreads / 16) * p;
     const uint16_t* src = w + (int64_t)r * ldw + col0;
     if (full) {
       v[p] = ld_stream16(src);
@@ -165,18 +169,20 @@ __device__ __forceinline__ void quant_blocks_body(int bid, const uint16_t* __res
   }
   uint32_t m = 0;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) m = max(m, absmax8(v[p]));
+  for (int p = 0; p < kRows; ++p) m = max(m, absmax8(v[p]));
   m = dpp_max16(m);
   m = max(max((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 16)),
           max((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
-  m = max(max(red[0], red[1]), max(red[2], red[3]));
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = max(m, red[i]);
 
   const TileScale ts = tile_scale<POW2>(m);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int r = row0 + r0 + 16 * p;
+  for (int p = 0; p < kRows; ++p) {
+    const int r = row0 + r0 + (kBlockThreads / 16) * p;
     const uint2 c = encode8<POW2>(v[p], ts);
     uint8_t* dst = codes + (int64_t)r * ldc + col0;
     if (full) {
@@ -189,7 +195,7 @@ __device__ __forceinline__ void quant_blocks_body(int bid, const uint16_t* __res
 }
 
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ w, int n,
+__global__ __launch_bounds__(kBlockThreads) void quant_blocks_kernel(const uint16_t* __restrict__ w, int n,
                                                            int k, int64_t ldw,
                                                            uint8_t* __restrict__ codes, int64_t ldc,
                                                            float* __restrict__ scales, int bk,
@@ -200,10 +206,11 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
 // ------------------------------- both operands of a linear layer at once ---
 // The activation's 1x128 tiles (the first `ga` workgroups, as in
 // quant_rows_kernel) and the weight's 128x128 blocks (one workgroup each, as
-// in quant_blocks_kernel) in one launch: one grid ramp and drain instead of
-// two, and the two streams overlap.
+// in quant_blocks_kernel) in one launch of 8-wave workgroups: one grid ramp
+// and drain instead of two, and the two streams overlap.
 template <bool PA, bool PW>
-__global__ __launch_bounds__(256) void quant_linear_kernel(const uint16_t* __restrict__ x, int cols, int64_t ldx,
+__global__ __launch_bounds__(kBlockThreads) void quant_linear_kernel(const uint16_t* __restrict__ x, int cols,
+                                                                     int64_t ldx,
                                                            uint8_t* __restrict__ a_codes, int64_t lda,
                                                            float* __restrict__ a_scales, int nb, int ntiles,
                                                            bool avec, int ga, const uint16_t* __restrict__ w,
@@ -530,8 +537,8 @@ __global__ __launch_bounds__(256) void quant_token_t_kernel(const uint16_t* __re
 // workgroups vs 5.8 TB/s with one pass for this 2:1 read:write stream).  The
 // row quantizer launches one-wave workgroups: 16.5 -> 16.0 us at 4096 x 7168
 // and 6.0 -> 5.75 us at 3773 x 2048 against four-wave ones (no change at
-// 16384 x 7168); the combined linear launch keeps four waves, which its
-// weight blocks need.
+// 16384 x 7168); the combined linear launch uses the 8-wave workgroups its
+// weight blocks take.
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx, bool pow2,
                              uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
@@ -550,7 +557,7 @@ hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, int64_t ldx,
 hipError_t launch_quant_blocks(const uint16_t* w, int n, int k, int64_t ldw, bool pow2,
                                uint8_t* codes, int64_t ldc, float* scales, hipStream_t stream) {
   const int bn = (n + 127) / 128, bk = (k + 127) / 128;
-  const dim3 grid(bn * bk), block(256);
+  const dim3 grid(bn * bk), block(kBlockThreads);
   const bool vec = ldw % 8 == 0 && ldc % 8 == 0;
   if (pow2) {
     hipLaunchKernelGGL(quant_blocks_kernel<true>, grid, block, 0, stream, w, n, k, ldw, codes, ldc, scales, bk, vec);
@@ -565,12 +572,12 @@ hipError_t launch_quant_linear(const uint16_t* x, int m, int k, int64_t ldx, boo
                                uint8_t* w_codes, int64_t ldwc, float* w_scales, hipStream_t stream) {
   const int nb = (k + 127) / 128;
   const int ntiles = m * nb;
-  const int ga = m > 0 ? rows_grid(ntiles) : 0;
+  const int ga = m > 0 ? rows_grid(ntiles, kBlockThreads / 4) : 0;
   const int bn = (n + 127) / 128;
   const int gw = n > 0 ? bn * nb : 0;
   const bool avec = ldx % 8 == 0 && lda % 8 == 0;
   const bool wvec = ldw % 8 == 0 && ldwc % 8 == 0;
-  const dim3 grid(ga + gw), block(256);
+  const dim3 grid(ga + gw), block(kBlockThreads);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, x, k, ldx, a_codes, lda, a_scales, nb, ntiles, avec, ga, w,
                        n, ldw, w_codes, ldwc, w_scales, nb, wvec);

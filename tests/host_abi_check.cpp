@@ -382,7 +382,7 @@ void large_sweeps() {
                            stream_tag()),
          FP8Q_ERR_SHAPE, false);
   for (int64_t ntiles : {int64_t(1), int64_t(63), int64_t(64), int64_t(1) << 26, rows, (int64_t(1) << 31) - 1}) {
-    for (int per_wg : {16, 64}) {  // one-wave and four-wave workgroups
+    for (int per_wg : {16, 128}) {  // one-wave and eight-wave workgroups
       const int g = fp8q::rows_grid(ntiles, per_wg);
       CHECK(g >= 1 && g <= fp8q::kMaxRowsGrid);
       CHECK(int64_t(g) * per_wg >= std::min<int64_t>(ntiles, int64_t(fp8q::kMaxRowsGrid) * per_wg));
