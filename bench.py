@@ -62,8 +62,8 @@ GEMM_MIN_BYTES = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 
 # traffic null.
 GEMM_TRAFFIC = {"bytes": 216190000,
                 "source_sha256": "a19cc29ec6707f5cb26530d1b19464ab9a58461561f37cec286ec4e3eddf38db",
-                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,416.9 KiB x 2.000 "
-                           "+ WRITE_SIZE 34,307.3 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
+                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,415.6 KiB x 2.000 "
+                           "+ WRITE_SIZE 34,305.0 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
 
 
 def parse():
