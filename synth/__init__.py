@@ -27,6 +27,10 @@ Recipes (seed 0; one child stream per tensor from
                  [sum M, 4096] (gate | up) ~N(0, 1.7): the spread of a sum
                  of 7168 N(0,1) x N(0, 0.02) products (sqrt(7168) * 0.02)
 
+* codes/scales:  uniformly drawn finite E4M3 codes and positive float32
+                 scales 2^U[-8, 8) * U[1, 2), for GEMM operands that are not
+                 the quantization of a BF16 input
+
 Outliers are multiplied in float32 before the BF16 rounding.  "N(0, 0.02)"
 is read as standard deviation 0.02.
 """
@@ -166,3 +170,21 @@ def reachable_band(ebits, seed):
         tiles.append(np.concatenate([head, xs], axis=1))
     return np.concatenate(tiles)
 
+
+
+def e4m3_codes(rng, shape):
+    """Uniformly drawn E4M3 bit patterns over the finite codes: the two NaN
+    patterns (0x7F, 0xFF) are replaced by the largest finite codes of the
+    same sign (0x7E, 0xFE), since no quantizer emits a NaN."""
+    n = int(np.prod(shape))
+    c = np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape).copy()
+    c[(c & 0x7F) == 0x7F] -= 1
+    return c
+
+
+def tile_scales(rng, shape):
+    """Positive float32 scales 2^e * m, e uniform in [-8, 8), m uniform in
+    [1, 2): free scales with full float32 mantissas."""
+    e = rng.integers(-8, 8, size=shape)
+    m = rng.uniform(1.0, 2.0, size=shape)
+    return (np.ldexp(m, e)).astype(np.float32)
