@@ -29,3 +29,16 @@ def test_moe_routing_has_an_empty_group_and_is_seeded():
     assert np.array_equal(c1, c2) and (c1 == 0).sum() >= 1
     assert all(np.all(np.diff(v) > 0) for v in l1)
     assert c1.max() <= 8192
+
+
+def test_random_codes_and_scales():
+    rng = np.random.default_rng(3)
+    c = synth.e4m3_codes(rng, (512, 1024))
+    counts = np.bincount(c.ravel(), minlength=256)
+    assert c.dtype == np.uint8 and c.shape == (512, 1024)
+    assert counts[0x7F] == 0 and counts[0xFF] == 0       # no NaN pattern
+    assert (counts[[b for b in range(256) if b & 0x7F != 0x7F]] > 0).all()  # every finite code drawn
+    assert np.array_equal(c, synth.e4m3_codes(np.random.default_rng(3), (512, 1024)))
+    s = synth.tile_scales(rng, (1000, 56))
+    assert s.dtype == np.float32 and (s >= 2.0 ** -8).all() and (s < 2.0 ** 8).all()
+    assert np.unique(s).size > 50000                      # free mantissas, not powers of two
