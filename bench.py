@@ -21,8 +21,9 @@ Timing:
     their inputs larger than the 256 MB Infinity Cache; `after_cache_flush`
     figures write 1 GiB before each launch.
 
-Prints one JSON line (contract fields first; `configs` holds every workload
-of the five configurations; `cpu_baseline` times the oracle on the host and
+Prints one JSON line (contract fields first; `workloads` holds every other
+workload: tiny linear, Dgrad, quantize-only sizes, MoE grouped GEMMs and
+glue, weight gradient; `cpu_baseline` times the oracle on the host and
 checks a sample of the timed step's outputs against it).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
@@ -247,7 +248,7 @@ def bf16_dev(torch, bits):
 
 
 def tiny_linear(torch, fp8q, lib, clock, sp):
-    """Config 1, 128 x 256 x 512, FP32 out: latency of one pass (quantize A and
+    """Tiny linear, 128 x 256 x 512, FP32 out: latency of one pass (quantize A and
     W in one launch, then the GEMM), and of each kernel."""
     import synth
     d = synth.tiny_linear()
@@ -274,7 +275,7 @@ def tiny_linear(torch, fp8q, lib, clock, sp):
 
 
 def quantize_only(torch, fp8q, lib, clock, sp, reps):
-    """Config 3: activations 16384 x 7168 (Student-t(3)) in both scale modes,
+    """Quantize-only sizes: activations 16384 x 7168 (Student-t(3)) in both scale modes,
     weights 7168 x 18432 per 128 x 128 block; two input/output sets, each
     larger than the Infinity Cache, alternate."""
     import synth
@@ -317,7 +318,7 @@ def quantize_only(torch, fp8q, lib, clock, sp, reps):
 
 
 def moe(torch, fp8q, lib, clock, sp, reps):
-    """Config 4, one GPU's share of the MoE layer: 8192 tokens routed top-8
+    """MoE grouped GEMMs, one GPU's share of the MoE layer: 8192 tokens routed top-8
     over 256 experts (Zipf(1.1) popularity), 16 hosted experts (one empty).
     Tokens are quantized once (1x128), their codes and scales gathered by
     expert (FP8 dispatch gather); grouped up-projection 7168 -> 4096 and
@@ -425,7 +426,7 @@ def moe(torch, fp8q, lib, clock, sp, reps):
 
 
 def wgrad(torch, fp8q, lib, clock, sp, reps):
-    """Config 5: dY 16384 x 2048 and X 16384 x 7168 (BF16 ~N(0,1)) quantized
+    """Weight gradient: dY 16384 x 2048 and X 16384 x 7168 (BF16 ~N(0,1)) quantized
     in 128-token x 1-feature tiles (codes feature-major), then
     dW[2048, 7168] = dY^T X in FP32."""
     import synth
@@ -513,7 +514,7 @@ def dgrad(torch, fp8q, lib, clock, sp, reps, w):
 
 def cpu_baseline(step_outputs):
     """The oracle, as it stands, on the host cores, on bounded samples of
-    each configuration (quantize and GEMM timed apart), and a parity check of
+    each workload (quantize and GEMM timed apart), and a parity check of
     a sample of the timed step's outputs against it.
 
     `value` is the oracle's block-scaled GEMM rate on the dense up-projection
@@ -537,7 +538,7 @@ def cpu_baseline(step_outputs):
         (qw, tqw) = timed(lambda: Q.quantize_blocks(d["w"]))
         (_, tg) = timed(lambda: G.gemm(qa[0], qa[1], qw[0], qw[1]))
         b1 = d["a"].size * 3.03125 + d["w"].size * 3.0
-        res["1_tiny_linear"] = {"quantize_s": round(tqa + tqw, 4), "quantize_GB/s": round(b1 / (tqa + tqw) / 1e9, 4),
+        res["tiny_linear_128x256x512"] = {"quantize_s": round(tqa + tqw, 4), "quantize_GB/s": round(b1 / (tqa + tqw) / 1e9, 4),
                                 "gemm_s": round(tg, 4), "gemm_TFLOP/s": round(2.0 * 128 * 256 * 512 / tg / 1e12, 6),
                                 "sample": "whole workload (A 128x512, W 256x512, C 128x256)"}
         # 2: dense up-projection, 2048 rows of A and of W
@@ -549,7 +550,7 @@ def cpu_baseline(step_outputs):
         (_, tg) = timed(lambda: G.gemm(qa[0], qa[1], qw[0], qw[1]))
         gemm2 = 2.0 * rows * rows * K / tg / 1e12
         b2 = a.size * 3.03125 + w.size * 3.0
-        res["2_dense_up"] = {"quantize_s": round(tqa + tqw, 3), "quantize_GB/s": round(b2 / (tqa + tqw) / 1e9, 4),
+        res["dense_up_4096x4096x7168"] = {"quantize_s": round(tqa + tqw, 3), "quantize_GB/s": round(b2 / (tqa + tqw) / 1e9, 4),
                              "gemm_s": round(tg, 3), "gemm_TFLOP/s": round(gemm2, 5),
                              "sample": f"A rows 0..{rows - 1}, W rows 0..{rows - 1}: GEMM {rows}x{rows}x{K}"}
         # 3: quantize-only, 4096 activation rows per mode and 2048 weight rows
@@ -558,7 +559,7 @@ def cpu_baseline(step_outputs):
         (_, tp) = timed(lambda: Q.quantize_rows(act, Q.POW2))
         wt = synth.quant_only_weight()[:2048]
         (_, tw) = timed(lambda: Q.quantize_blocks(wt))
-        res["3_quantize_only"] = {"act_free_GB/s": round(act.size * 3.03125 / tf / 1e9, 4),
+        res["quantize_only"] = {"act_free_GB/s": round(act.size * 3.03125 / tf / 1e9, 4),
                                   "act_pow2_GB/s": round(act.size * 3.03125 / tp / 1e9, 4),
                                   "weight_GB/s": round(wt.size * 3.0 / tw / 1e9, 4),
                                   "seconds": round(tf + tp + tw, 3),
@@ -571,7 +572,7 @@ def cpu_baseline(step_outputs):
         (qx, tq) = timed(lambda: Q.quantize_rows(xr))
         (qwe, tqw) = timed(lambda: Q.quantize_blocks(md["w_up"][e][:2048]))
         (_, tg) = timed(lambda: G.gemm(qx[0], qx[1], qwe[0], qwe[1]))
-        res["4_moe_grouped"] = {"quantize_s": round(tq + tqw, 3), "gemm_s": round(tg, 3),
+        res["moe_grouped_16_experts"] = {"quantize_s": round(tq + tqw, 3), "gemm_s": round(tg, 3),
                                 "gemm_TFLOP/s": round(2.0 * xr.shape[0] * 2048 * xr.shape[1] / tg / 1e12, 5),
                                 "sample": f"expert {e}: {xr.shape[0]} of its rows x 2048 of its 4096 up-projection columns"}
         del md
@@ -581,7 +582,7 @@ def cpu_baseline(step_outputs):
         (qx5, tq2) = timed(lambda: Q.quantize_token_t(np.ascontiguousarray(wd["x"][:, :1024])))
         (_, tg) = timed(lambda: G.wgrad(qdy[0], qdy[1], qx5[0], qx5[1]))
         t_tok = wd["dy"].shape[0]
-        res["5_wgrad"] = {"quantize_s": round(tq1 + tq2, 3),
+        res["wgrad_2048x7168x16384"] = {"quantize_s": round(tq1 + tq2, 3),
                           "quantize_GB/s": round(t_tok * 1280 * 3.03125 / (tq1 + tq2) / 1e9, 4),
                           "gemm_s": round(tg, 3), "gemm_TFLOP/s": round(2.0 * 256 * 1024 * t_tok / tg / 1e12, 5),
                           "sample": f"dW[0:256, 0:1024] over {t_tok} tokens"}
@@ -589,10 +590,10 @@ def cpu_baseline(step_outputs):
         parity = step_parity(step_outputs, synth, Q, G)
     total = sum(v.get("seconds", v.get("quantize_s", 0) + v.get("gemm_s", 0)) for v in res.values())
     blas = [i.get("num_threads") for i in threadpoolctl.threadpool_info()]
-    return {"value": res["2_dense_up"]["gemm_TFLOP/s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": res["dense_up_4096x4096x7168"]["gemm_TFLOP/s"], "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "the oracle's block-scaled GEMM on 2048 rows of A and W of the 4096x4096x7168 workload "
-                      f"(value); every configuration's sample timed apart in per_config ({total:.1f} s in all)",
-            "blas_threads": blas, "per_config": res, "parity_on_timed_outputs": parity}
+                      f"(value); every workload's sample timed apart in per_workload ({total:.1f} s in all)",
+            "blas_threads": blas, "per_workload": res, "parity_on_timed_outputs": parity}
 
 
 def step_parity(outs, synth, Q, G):
@@ -797,17 +798,17 @@ def main():
     del ap_c, ap_s, wp_c, wp_s
     clock.release()
 
-    progress("config 2 (timed steps, quantizers, GEMM forms) done")
-    configs = {"1_tiny_linear": tiny_linear(torch, fp8q, lib, clock, sp), "2_dense_up": dense}
-    progress("config 1 done")
-    configs["dgrad_of_2"] = dgrad(torch, fp8q, lib, clock, sp, reps, w)
+    progress("dense up-projection (timed steps, quantizers, GEMM forms) done")
+    workloads = {"tiny_linear_128x256x512": tiny_linear(torch, fp8q, lib, clock, sp), "dense_up_4096x4096x7168": dense}
+    progress("tiny linear done")
+    workloads["dgrad_4096x7168x4096"] = dgrad(torch, fp8q, lib, clock, sp, reps, w)
     progress("Dgrad done")
-    configs["3_quantize_only"] = quantize_only(torch, fp8q, lib, clock, sp, reps)
-    progress("config 3 done")
-    configs["4_moe_grouped"] = moe(torch, fp8q, lib, clock, sp, reps)
-    progress("config 4 done")
-    configs["5_wgrad"] = wgrad(torch, fp8q, lib, clock, sp, reps)
-    progress("config 5 done")
+    workloads["quantize_only"] = quantize_only(torch, fp8q, lib, clock, sp, reps)
+    progress("quantize-only sizes done")
+    workloads["moe_grouped_16_experts"] = moe(torch, fp8q, lib, clock, sp, reps)
+    progress("MoE grouped done")
+    workloads["wgrad_2048x7168x16384"] = wgrad(torch, fp8q, lib, clock, sp, reps)
+    progress("Wgrad done")
 
     traffic = GEMM_TRAFFIC["bytes"] if GEMM_TRAFFIC["source_sha256"] == source_sha256("gemm.hip") else None
     achieved = GEMM_FLOP / gemm_live_us / 1e6
@@ -843,7 +844,7 @@ def main():
                      "traffic_source": (GEMM_TRAFFIC["profile"] if traffic is not None else
                                         "null: the kernel source changed since the counters were taken")},
         "cpu_baseline": None,
-        "configs": configs,
+        "workloads": workloads,
         "pages_context": {
             "accumulation_interval_elements": 128,
             "accumulation_interval_hardware": "H800 tensor cores, four WGMMAs (jp-study.kr doc 258368, 3rd paragraph)",
