@@ -56,12 +56,16 @@ def accumulate(terms, interval, width=None):
     return out.astype(np.float64)
 
 
+def dequantize(codes_rows, scales_rows):
+    """Values q*s (float64 [S, K]) of code rows with one scale per
+    128-element block (scales_rows [S, K/128])."""
+    from .e4m3 import decode
+    return decode(codes_rows) * np.repeat(np.asarray(scales_rows, np.float64), 128, axis=1)
+
+
 def dequantized_products(a_codes_rows, a_scales_rows, b_codes_rows, b_scales_rows):
     """Products (qa*sa)(qb*sb) along K for paired rows (float64 [S, K]).
 
     a_scales_rows / b_scales_rows are per 128-element block ([S, K/128]).
     """
-    from .e4m3 import decode
-    a = decode(a_codes_rows) * np.repeat(np.asarray(a_scales_rows, np.float64), 128, axis=1)
-    b = decode(b_codes_rows) * np.repeat(np.asarray(b_scales_rows, np.float64), 128, axis=1)
-    return a * b
+    return dequantize(a_codes_rows, a_scales_rows) * dequantize(b_codes_rows, b_scales_rows)

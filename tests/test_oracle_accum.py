@@ -44,3 +44,21 @@ def test_truncation_toward_zero_alignment():
     # the 2^-23 grid toward zero -> -0.75, so the sum is exactly 0.75
     terms = np.array([[1.5, -0.75 - 2.0 ** -25]])
     assert accum.accumulate(terms, interval=2, width=24)[0] == 0.75
+
+
+def test_dequantized_products_hand_values():
+    # E4M3: 0x38 = 1.0, 0x01 = 2^-9 (smallest subnormal), 0xC4 = -3.0,
+    # 0x7E = 448; one scale per 128-element block
+    a = np.zeros((1, 256), np.uint8)
+    b = np.zeros((1, 256), np.uint8)
+    a[0, :4] = [0x38, 0x01, 0xC4, 0x7E]
+    b[0, :4] = [0x38, 0x38, 0x38, 0x01]
+    a[0, 128] = 0x38
+    b[0, 128] = 0xC4
+    sa = np.array([[0.5, 4.0]], np.float32)
+    sb = np.array([[2.0, 0.25]], np.float32)
+    da = accum.dequantize(a, sa)
+    assert da[0, :4].tolist() == [0.5, 2.0 ** -10, -1.5, 224.0] and da[0, 128] == 4.0
+    p = accum.dequantized_products(a, sa, b, sb)
+    assert p[0, :4].tolist() == [1.0, 2.0 ** -9, -3.0, 224.0 * 2.0 ** -8] and p[0, 128] == -3.0
+    assert not p[0, 4:128].any() and not p[0, 129:].any()
