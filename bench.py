@@ -425,14 +425,22 @@ def moe(torch, fp8q, lib, clock, sp, reps):
     return out
 
 
-def wgrad(torch, fp8q, lib, clock, sp, reps):
+def wgrad(torch, fp8q, lib, clock, sp, reps, sample=None):
     """Weight gradient: dY 16384 x 2048 and X 16384 x 7168 (BF16 ~N(0,1)) quantized
     in 128-token x 1-feature tiles (codes feature-major), then
-    dW[2048, 7168] = dY^T X in FP32."""
+    dW[2048, 7168] = dY^T X in FP32.
+
+    With `sample` = (dW rows, dW columns), also returns what the GPU computed
+    there for the promotion study: dW of every accumulation form and the
+    sampled features' codes and scales (free and power-of-two)."""
     import synth
     d = synth.wgrad()
     out = {}
     q = {}
+    study = None
+    if sample is not None:
+        rs, cs = (torch.as_tensor(v, device="cuda:0") for v in sample)
+        study = {"dw": {}, "operands": {}}
     for name, arr in (("dy", d["dy"]), ("x", d["x"])):
         t = bf16_dev(torch, arr)
         tok, feat = t.shape
@@ -451,6 +459,10 @@ def wgrad(torch, fp8q, lib, clock, sp, reps):
         del t, t2
     dyc, dys, T, nout, dyc2, dys2 = q["dy"]
     xc, xs, _, kin, xc2, xs2 = q["x"]
+    if study is not None:
+        for mode, ops in (("free", (dyc, dys, xc, xs)), ("pow2", (dyc2, dys2, xc2, xs2))):
+            study["operands"][mode] = {k: v.cpu().numpy() for k, v in zip(
+                ("dyc", "dys", "xc", "xs"), (ops[0][rs], ops[1][rs], ops[2][cs], ops[3][cs]))}
     dw = torch.empty((nout, kin), dtype=torch.float32, device="cuda:0")
     flop = 2.0 * nout * kin * T
     nbytes = (nout + kin) * T + (nout + kin) * (T // 128) * 4 + nout * kin * 4
@@ -465,7 +477,10 @@ def wgrad(torch, fp8q, lib, clock, sp, reps):
         r = clock.stats(fg, reps, flop=flop, nbytes=nbytes)
         r.update(roofline_entry(flop, nbytes, r.get("batch_avg_us", r["median_us"])))
         out[f"wgrad_{nout}x{kin}x{T}{acc_name}"] = r
-    return out
+        if study is not None:
+            assert fg(0) == 0
+            study["dw"][acc_name] = dw[rs][:, cs].cpu().numpy().astype(np.float64)
+    return out, study
 
 
 def dgrad(torch, fp8q, lib, clock, sp, reps, w):
@@ -596,6 +611,54 @@ def cpu_baseline(step_outputs):
             "blas_threads": blas, "per_workload": res, "parity_on_timed_outputs": parity}
 
 
+def promotion_emulators():
+    """Promotion-interval study, CPU part (run before the GPU is opened: its
+    worker processes are forks of this one).  On the seeded 65,536-element
+    sample of dW of the weight-gradient workload (256 rows x 256 columns),
+    the oracle's quantization and exact values (free and power-of-two
+    scales) and its accumulation emulators on the free-scale operands: a
+    float32 accumulator and 13/14/16/20-bit fixed-point ones, each promoted
+    to float32 every 128 products and not at all."""
+    import synth
+    from oracle import quantize as Q
+    from tests import promotion_sample as P
+
+    t0 = time.perf_counter()
+    d = synth.wgrad()
+    t = d["dy"].shape[0]
+    ops = {"free": P.operands(d, Q.FREE), "pow2": P.operands(d, Q.POW2)}
+    del d
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    configs = P.emulator_configs(t)
+    sums = P.emulate(ops["free"], configs, workers)
+    emulated = {name: P.stats(sums[name], ops["free"]["exact"], ops["free"]["s"]) for name, _, _ in configs}
+    return {"ops": ops, "emulated": emulated, "seconds": round(time.perf_counter() - t0, 1), "workers": workers}
+
+
+def promotion_report(cpu, gpu):
+    """The promotion study: the GPU's accumulation forms on the weight-
+    gradient workload against the exact dW on the sample, next to the
+    emulators (promotion every 128 elements: jp-study.kr doc 258368, 3rd
+    paragraph)."""
+    from tests import promotion_sample as P
+
+    same = all(np.array_equal(np.asarray(gpu["operands"][m][k]).view(np.uint8),
+                              np.asarray(cpu["ops"][m][k]).view(np.uint8))
+               for m in ("free", "pow2") for k in ("dyc", "dys", "xc", "xs"))
+    forms = {"interval_128_fp32_grade": ("free", ""), "interval_128_fp8_unit": ("free", "_fp8_mfma"),
+             "pow2_no_promotion_fp32_grade": ("pow2", "_fp32_pow2"),
+             "pow2_no_promotion_fp8_unit_hardware_scales": ("pow2", "_fp8_mfma_scaled_pow2")}
+    return {"workload": "dW 2048x7168 over 16384 tokens (128-token tiles)",
+            "sample": f"{P.SIDE} dW rows x {P.SIDE} columns = {P.SIDE * P.SIDE} elements (seed 2024)",
+            "errors": "max and mean of |value - exact| / sum|a b|, median of |value - exact| / |exact|, "
+                      "fraction within 1e-5 sum|a b| + 1e-6",
+            "gpu_codes_and_scales_equal_oracle_on_sample": bool(same),
+            "gpu": {name: P.stats(gpu["dw"][key], cpu["ops"][mode]["exact"], cpu["ops"][mode]["s"])
+                    for name, (mode, key) in forms.items()},
+            "emulated": cpu["emulated"],
+            "emulator_seconds": cpu["seconds"], "emulator_workers": cpu["workers"]}
+
+
 def step_parity(outs, synth, Q, G):
     """A sample of the timed step's outputs against the oracle: 16 rows of A
     and two 128-row weight blocks, codes and scales bit for bit, and the
@@ -651,6 +714,12 @@ def main():
         print(json.dumps({"error": "fp8q runs on one GPU only: it has no multi-GPU path (no sharding, no "
                                    "collectives); run with --gpus 1"}))
         sys.exit(2)
+
+    # the promotion study's CPU part forks worker processes: before torch
+    # opens the GPU
+    study_cpu = None if args.no_cpu_baseline else promotion_emulators()
+    if study_cpu is not None:
+        progress(f"promotion-study emulators done ({study_cpu['seconds']} s)")
 
     import torch
     import fine_grained_fp8_fp8q_amd as fp8q
@@ -807,7 +876,8 @@ def main():
     progress("quantize-only sizes done")
     workloads["moe_grouped_16_experts"] = moe(torch, fp8q, lib, clock, sp, reps)
     progress("MoE grouped done")
-    workloads["wgrad_2048x7168x16384"] = wgrad(torch, fp8q, lib, clock, sp, reps)
+    sample = None if study_cpu is None else (study_cpu["ops"]["free"]["rsel"], study_cpu["ops"]["free"]["csel"])
+    workloads["wgrad_2048x7168x16384"], study_gpu = wgrad(torch, fp8q, lib, clock, sp, reps, sample)
     progress("Wgrad done")
 
     traffic = GEMM_TRAFFIC["bytes"] if GEMM_TRAFFIC["source_sha256"] == source_sha256("gemm.hip") else None
@@ -856,6 +926,7 @@ def main():
     if not args.no_cpu_baseline:
         progress("timing the oracle on the host cores")
         out["cpu_baseline"] = cpu_baseline(step_outputs)
+        out["promotion_study"] = promotion_report(study_cpu, study_gpu)
     print(json.dumps(out), flush=True)
 
 

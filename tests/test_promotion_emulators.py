@@ -20,34 +20,14 @@ FP8Q_EMULATOR_OUT names a file, written there as JSON.
 """
 
 import json
-import multiprocessing
 import os
 import sys
-from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 import pytest
 
 import synth
-from oracle import accum
 from tests import promotion_sample as P
-
-WIDTHS = (13, 14, 16, 20)
-CHUNK = 8192  # sampled elements per worker task (its products take 1 GiB)
-
-# set before the worker processes fork (they read them, copy-on-write)
-_SHARED = {}
-
-
-def _emulate(lo):
-    """Every emulator on sampled elements lo .. lo + CHUNK - 1."""
-    a, b, ri, ci, configs = (_SHARED[k] for k in ("a", "b", "ri", "ci", "configs"))
-    r, c = ri[lo:lo + CHUNK], ci[lo:lo + CHUNK]
-    # the products (a sa)(b sb) of each sampled pair, as
-    # accum.dequantized_products forms them; one column per product index,
-    # so each accumulation step reads contiguous memory
-    terms = np.asfortranarray(a[r] * b[c])
-    return lo, {name: accum.accumulate(terms, interval, width) for name, interval, width in configs}
 
 
 @pytest.mark.slow
@@ -56,22 +36,9 @@ def test_promotion_emulators():
     t = d["dy"].shape[0]
     ops = P.operands(d)
     del d
-    ri = np.repeat(np.arange(P.SIDE), P.SIDE)
-    ci = np.tile(np.arange(P.SIDE), P.SIDE)
-    configs = [("fp32_interval_128", 128, None), ("fp32_no_promotion", t, None)]
-    for w in WIDTHS:
-        configs += [(f"fixed{w}_interval_128", 128, w), (f"fixed{w}_no_promotion", t, w)]
-    # the 256 sampled dY and X rows dequantized once (the sample pairs them)
-    _SHARED.update(a=accum.dequantize(ops["dyc"], ops["dys"]), b=accum.dequantize(ops["xc"], ops["xs"]),
-                   ri=ri, ci=ci, configs=configs)
-    sums = {name: np.empty(ri.size) for name, _, _ in configs}
-    workers = max(1, min(8, len(os.sched_getaffinity(0))))
-    with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("fork")) as pool:
-        for lo, part in pool.map(_emulate, range(0, ri.size, CHUNK)):
-            for name, v in part.items():
-                sums[name][lo:lo + CHUNK] = v
-    _SHARED.clear()
-    report = {"workload": f"dW 2048x7168, T={t}, sample {P.SIDE}x{P.SIDE} = {ri.size} elements"}
+    configs = P.emulator_configs(t)
+    sums = P.emulate(ops, configs, workers=max(1, min(8, len(os.sched_getaffinity(0)))))
+    report = {"workload": f"dW 2048x7168, T={t}, sample {P.SIDE}x{P.SIDE} = {P.SIDE * P.SIDE} elements"}
     for name, _, _ in configs:
         report[f"emulated_{name}"] = P.stats(sums[name], ops["exact"], ops["s"])
     print(json.dumps(report, indent=1), file=sys.stderr)
@@ -85,9 +52,9 @@ def test_promotion_emulators():
     # promotion is what keeps a narrow accumulator usable: at every width the
     # promoted sum is more accurate than the unpromoted one, and a wider
     # accumulator is more accurate than a narrower one
-    for w in WIDTHS:
+    for w in P.WIDTHS:
         assert (report[f"emulated_fixed{w}_interval_128"]["mean_err_over_S"]
                 < report[f"emulated_fixed{w}_no_promotion"]["mean_err_over_S"])
-    for lo_w, hi_w in zip(WIDTHS, WIDTHS[1:]):
+    for lo_w, hi_w in zip(P.WIDTHS, P.WIDTHS[1:]):
         assert (report[f"emulated_fixed{hi_w}_interval_128"]["mean_err_over_S"]
                 < report[f"emulated_fixed{lo_w}_interval_128"]["mean_err_over_S"])
