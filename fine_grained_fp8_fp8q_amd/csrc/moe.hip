@@ -63,9 +63,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 // which neither overflows nor loses the tail for large negative g:
 // sigma(g) = 1 / (1 + t) for g >= 0 and t / (1 + t) for g < 0.  1 + t lies
 // in [1, 2], where the hardware reciprocal is within 1 ulp.
-// e^x for x <= 0: x log2(e) = n + f with |f| <= 1/2 (log2(e) carried in two
-// parts), 2^f from the hardware exp2, scaled by 2^n with ldexp (which also
-// rounds subnormal results); below -104 the result is 0.
+// e^x for x <= 0: x log2(e) = n + f with |f| <= 1/2, reduced with log2(e)
+// carried as a float32 head and a small tail (Cody and Waite's two-constant
+// argument reduction, taken in base 2), 2^f from the hardware exp2, scaled by
+// 2^n with ldexp (which also rounds subnormal results); below -104 the
+// result is 0.
 __device__ __forceinline__ float exp_nonpos(float x) {
   x = __builtin_fmaxf(x, -104.0f);
   const float l2e_hi = 1.44269502162933349609375f;  // RN32(log2 e)
