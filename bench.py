@@ -247,9 +247,39 @@ def bf16_dev(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
+def graph_replay_us(torch, fn, reps=20, min_ms=100.0, replays=50):
+    """GPU time (us) per call of fn(stream), from a HIP graph holding `reps`
+    calls, replayed back to back (after `min_ms` of untimed replays) under one
+    event pair: without the host's cost of each call, which for a kernel of a
+    few microseconds is longer than the kernel itself."""
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for _ in range(reps):
+            if fn(gs.cuda_stream) != 0:
+                raise RuntimeError("fp8q call failed during graph capture")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        g.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    e1.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / (reps * replays), 2), g
+
+
 def tiny_linear(torch, fp8q, lib, clock, sp):
     """Tiny linear, 128 x 256 x 512, FP32 out: latency of one pass (quantize A and
-    W in one launch, then the GEMM), and of each kernel."""
+    W in one launch, then the GEMM), and of each kernel.  Launched one call at a
+    time from the host, a pass of a few microseconds is timed as the host's call
+    rate; `graph_replay` gives the GPU's own time per pass (and per kernel) from
+    HIP graphs of 20 passes, and checks that a replayed pass writes exactly what
+    the eager pass wrote."""
     import synth
     d = synth.tiny_linear()
     a, w = bf16_dev(torch, d["a"]), bf16_dev(torch, d["w"])
@@ -258,20 +288,40 @@ def tiny_linear(torch, fp8q, lib, clock, sp):
     ac, as_, wc, ws = fp8q.quantize_linear(a, w)
     c = torch.empty((m, n), dtype=torch.float32, device="cuda:0")
 
-    def q(i):
+    def q_on(s):
         return lib.fp8q_quantize_linear(a.data_ptr(), m, k, k, fp8q.SCALE_FREE, ac.data_ptr(), ac.stride(0),
                                         as_.data_ptr(), w.data_ptr(), n, k, fp8q.SCALE_FREE, wc.data_ptr(),
-                                        wc.stride(0), ws.data_ptr(), sp)
+                                        wc.stride(0), ws.data_ptr(), s)
 
-    def g(i):
+    def g_on(s):
         return lib.fp8q_gemm(ac.data_ptr(), as_.data_ptr(), wc.data_ptr(), ws.data_ptr(), m, n, k, fp8q.OUT_F32,
-                             c.data_ptr(), n, sp)
+                             c.data_ptr(), n, s)
 
-    def step(i):
-        return q(i) or g(i)
-    return {"workload": "tiny linear: quantize A 128x512 (1x128) + W 256x512 (128x128), GEMM -> FP32 [128, 256]",
-            "step_latency": clock.stats(step, 200), "quantize_linear": clock.stats(q, 200),
-            "gemm": clock.stats(g, 200, flop=2.0 * m * n * k)}
+    def step_on(s):
+        return q_on(s) or g_on(s)
+
+    res = {"workload": "tiny linear: quantize A 128x512 (1x128) + W 256x512 (128x128), GEMM -> FP32 [128, 256]",
+           "step_latency": clock.stats(lambda i: step_on(sp), 200),
+           "quantize_linear": clock.stats(lambda i: q_on(sp), 200),
+           "gemm": clock.stats(lambda i: g_on(sp), 200, flop=2.0 * m * n * k)}
+    # the eager pass's output, then the same pass replayed from a graph
+    if step_on(sp) != 0:
+        raise RuntimeError("fp8q call failed")
+    torch.cuda.synchronize()
+    want = (ac.clone(), as_.clone(), wc.clone(), ws.clone(), c.clone())
+    for t in (ac, as_, wc, ws, c):
+        t.zero_()
+    step_us, graph = graph_replay_us(torch, step_on)
+    got = (ac, as_, wc, ws, c)
+    same = all(torch.equal(x.view(torch.uint8), y.view(torch.uint8)) for x, y in zip(got, want))
+    del graph
+    q_us, _ = graph_replay_us(torch, q_on)
+    g_us, _ = graph_replay_us(torch, g_on)
+    res["graph_replay"] = {"step_us": step_us, "quantize_linear_us": q_us, "gemm_us": g_us,
+                           "gemm_TFLOP/s": round(2.0 * m * n * k / g_us / 1e6, 1),
+                           "passes_per_graph": 20, "replays_timed": 50,
+                           "replayed_outputs_identical_to_eager": bool(same)}
+    return res
 
 
 def quantize_only(torch, fp8q, lib, clock, sp, reps):

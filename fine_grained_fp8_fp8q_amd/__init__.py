@@ -43,7 +43,7 @@ TILE_ROW, TILE_TOKEN_T = 0, 1
 
 SYMBOLS = ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_quantize_linear", "fp8q_quantize_weight_t", "fp8q_gemm",
            "fp8q_gemm_ex", "fp8q_gemm_quantized", "fp8q_grouped_gemm", "fp8q_grouped_gemm_ex", "fp8q_wgrad",
-           "fp8q_wgrad_ex", "fp8q_gather_rows", "fp8q_swiglu_quantize",
+           "fp8q_wgrad_ex", "fp8q_gather_rows", "fp8q_swiglu_quantize", "fp8q_set_gemm_small_limit",
            "fp8q_status_string")
 
 _lib = None
@@ -78,7 +78,9 @@ def load_library(path=None):
     lib.fp8q_wgrad_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, ip, vp, i64, vp]
     lib.fp8q_gather_rows.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, i64, vp, vp]
     lib.fp8q_swiglu_quantize.argtypes = [vp, i64, i64, i64, ip, vp, i64, vp, ip, vp, i64, vp, vp]
-    for name in SYMBOLS[:-1]:
+    lib.fp8q_set_gemm_small_limit.argtypes = [i64]
+    lib.fp8q_set_gemm_small_limit.restype = i64
+    for name in SYMBOLS[:-2]:
         getattr(lib, name).restype = ctypes.c_int
     lib.fp8q_status_string.argtypes = [ctypes.c_int]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -297,6 +299,13 @@ def gemm(a, a_scales, w, w_scales, out_dtype=None, out=None, acc="fp32"):
                               _ptr(c), c.stride(0), _stream(a))
     _check(st, "fp8q_gemm")
     return c
+
+
+def set_gemm_small_limit(max_outputs):
+    """Outputs (M * N) up to which the float32-grade dense GEMM uses 32 x 32
+    split-K tiles; a negative value restores the default.  Returns the
+    previous setting (-1 for the default)."""
+    return int(load_library().fp8q_set_gemm_small_limit(int(max_outputs)))
 
 
 def gemm_quantized(a, a_scales, w, w_scales, scale_mode="free", acc="fp32"):

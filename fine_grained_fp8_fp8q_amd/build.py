@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfp8q.so")
 # the bench's plain streaming kernel (a measuring stick, not part of libfp8q)
 STREAMREF_LIB = os.path.join(PKG, "libfp8q_streamref.so")
 
-SOURCES = ["quant.hip", "gemm.hip", "moe.hip", "fp8q_api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_small.hip", "moe.hip", "fp8q_api.cpp"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly (the quotient correction and the scale fold depend on it).

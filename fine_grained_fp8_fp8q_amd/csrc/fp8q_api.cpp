@@ -177,6 +177,8 @@ fp8q_status fp8q_gemm_ex(const uint8_t* a, const float* a_scales, const uint8_t*
                                     out_dtype == FP8Q_OUT_BF16, acc, c, ld_c, stream));
 }
 
+int64_t fp8q_set_gemm_small_limit(int64_t max_outputs) { return fp8q::set_small_gemm_limit(max_outputs); }
+
 fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype, void* c, int64_t ld_c, hipStream_t stream) {
   return fp8q_gemm_ex(a, a_scales, w, w_scales, M, N, K, out_dtype, FP8Q_ACC_FP32, c, ld_c, stream);

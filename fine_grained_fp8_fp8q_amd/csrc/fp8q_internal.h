@@ -47,6 +47,17 @@ hipError_t launch_quant_blocks_t(const uint16_t* w, int n, int k, int64_t ldw, b
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                        const float* w_scales, int m, int n, int k, bool bf16_out, int acc,
                        void* c, int64_t ldc, hipStream_t stream);
+// float32-grade dense GEMM over 32 x 32 output tiles with the K blocks split
+// over four waves (gemm_small.hip); launch_gemm takes it for outputs of at
+// most small_gemm_limit() elements
+hipError_t launch_gemm_small(const uint8_t* a, const float* a_scales, const uint8_t* w, const float* w_scales,
+                             int m, int n, int k, bool bf16_out, void* c, int64_t ldc, hipStream_t stream);
+// outputs (M * N) up to which the dense float32-grade GEMM uses the small
+// kernel: the value set by set_small_gemm_limit, or, while none is set (or
+// after a negative one), 8192 per compute unit of the current device
+int64_t small_gemm_limit();
+int64_t set_small_gemm_limit(int64_t max_outputs);  // returns the previous setting (-1: the default)
+int device_cus();
 // C = A . W^T rounded to BF16, quantized per 1x128 tile along N
 hipError_t launch_gemm_quantized(const uint8_t* a, const float* a_scales, const uint8_t* w,
                                  const float* w_scales, int m, int n, int k, int acc, bool pow2,

@@ -941,22 +941,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bs_kernel(GemmArgs g) {
   }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
-  if (dev >= 0 && dev < kMaxDevices) {
-    if (const int c = cache[dev].load(std::memory_order_relaxed)) return c;
-  }
-  int n = 0;
-  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 // Tile width in N for a dense or weight-gradient launch.  One tile per CU
 // and round of tiles, so the time goes as (rounds of tiles) x (tile width);
 // 224 columns when that is smaller.  The 2048 x 7168 weight gradient has 224
@@ -999,9 +983,43 @@ hipError_t launch_acc(const GemmArgs& g, int grid, int acc, hipStream_t stream) 
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    if (const int c = cache[dev].load(std::memory_order_relaxed)) return c;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Outputs up to which the dense float32-grade GEMM runs the 32 x 32 split-K
+// kernel (-1: the default, 8192 per compute unit, i.e. as many outputs as
+// an eighth of the compute units hold in 256 x 256 tiles).
+namespace {
+std::atomic<int64_t> g_small_limit{-1};
+}
+
+int64_t small_gemm_limit() {
+  const int64_t v = g_small_limit.load(std::memory_order_relaxed);
+  return v >= 0 ? v : (int64_t)device_cus() * 8192;
+}
+
+int64_t set_small_gemm_limit(int64_t max_outputs) {
+  return g_small_limit.exchange(max_outputs < 0 ? -1 : max_outputs, std::memory_order_relaxed);
+}
+
 hipError_t launch_gemm(const uint8_t* a, const float* a_scales, const uint8_t* w,
                        const float* w_scales, int m, int n, int k, bool bf16_out, int acc,
                        void* c, int64_t ldc, hipStream_t stream) {
+  if (acc == 0 && (int64_t)m * n <= small_gemm_limit())
+    return launch_gemm_small(a, a_scales, w, w_scales, m, n, k, bf16_out, c, ldc, stream);
   GemmArgs g{};
   g.a = a; g.sa = a_scales; g.w = w; g.sw = w_scales; g.offsets = nullptr;
   g.c = c; g.ldc = ldc; g.vec_c = (ldc % 4) == 0; g.rows = m; g.n = n; g.k = k; g.groups = 1;

@@ -188,6 +188,21 @@ fp8q_status fp8q_gemm(const uint8_t* a, const float* a_scales,
                       int64_t M, int64_t N, int64_t K, int out_dtype,
                       void* c, int64_t ld_c, hipStream_t stream);
 
+/* Tiling of the dense float32-grade GEMM (fp8q_gemm, and fp8q_gemm_ex with
+ * FP8Q_ACC_FP32), for outputs too small to fill the compute units with
+ * 256-wide tiles (a linear layer over a few hundred tokens): an output of at
+ * most max_outputs elements (M * N) runs on 32 x 32 tiles whose K blocks are
+ * split over the four waves of a workgroup and added in a fixed order;
+ * larger outputs run on 256 x 256 (or 256 x 224) tiles, each over the whole
+ * of K.  Both satisfy the bound stated for fp8q_gemm; they may differ from
+ * each other by the float32 rounding of the summation order.  The other
+ * accumulation forms always take the large tiles.  Default, and after any
+ * negative value: 8192 outputs per compute unit of the device a launch runs
+ * on (as many outputs as an eighth of the compute units hold in 256 x 256
+ * tiles).  Process-wide and atomic; launches issued after the call see the
+ * new value.  Returns the previous setting (-1 for the default). */
+int64_t fp8q_set_gemm_small_limit(int64_t max_outputs);
+
 /* fp8q_gemm with the accumulation form chosen by the caller: acc is one of
  * the FP8Q_ACC_* values above (fp8q_gemm is fp8q_gemm_ex with
  * FP8Q_ACC_FP32).  Same arguments, layouts and errors otherwise; an unknown
@@ -201,12 +216,14 @@ fp8q_status fp8q_gemm_ex(const uint8_t* a, const float* a_scales,
  * takes FP8 input (tmdrlife.com wr_id=13334 ¶1: the BF16 output of one
  * computation is read back from HBM only to be quantized, written as FP8 and
  * read again for the next MMA; here the producer writes the FP8 form
- * directly).  C is formed exactly as fp8q_gemm forms it (acc as there),
- * rounded to BF16 (nearest even) as with FP8Q_OUT_BF16, and that BF16 tensor
- * is quantized per 1x128 tile along N exactly as fp8q_quantize_act
- * (FP8Q_TILE_ROW, scale_mode) quantizes it: the result is bit for bit the
- * unfused fp8q_gemm(FP8Q_OUT_BF16) followed by fp8q_quantize_act, without
- * the BF16 round trip through HBM.
+ * directly).  C is formed exactly as fp8q_gemm forms it on 256-wide tiles
+ * (acc as there), rounded to BF16 (nearest even) as with FP8Q_OUT_BF16, and
+ * that BF16 tensor is quantized per 1x128 tile along N exactly as
+ * fp8q_quantize_act (FP8Q_TILE_ROW, scale_mode) quantizes it: the result is
+ * bit for bit the unfused fp8q_gemm(FP8Q_OUT_BF16) -- on 256-wide tiles,
+ * which it takes for every output larger than the limit of
+ * fp8q_set_gemm_small_limit -- followed by fp8q_quantize_act, without the
+ * BF16 round trip through HBM.
  * a, a_scales, w, w_scales, M, N, K as for fp8q_gemm, acc as for fp8q_gemm_ex; c_codes
  * [M, ld_c >= N] E4M3; c_scales [M, ceil(N/128)] float32. */
 fp8q_status fp8q_gemm_quantized(const uint8_t* a, const float* a_scales,

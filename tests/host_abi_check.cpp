@@ -123,6 +123,12 @@ hipError_t launch_swiglu_quant(const uint16_t* x, int rows, int inter, int64_t l
   return record("swiglu_quant", {rows, inter, ldx, pow2, ldc, cache_pow2, ldcc},
                 {x, codes, scales, ccodes, cscales}, s);
 }
+int64_t g_small_limit_stub = -1;
+int64_t set_small_gemm_limit(int64_t max_outputs) {
+  const int64_t prev = g_small_limit_stub;
+  g_small_limit_stub = max_outputs < 0 ? -1 : max_outputs;
+  return prev;
+}
 
 }  // namespace fp8q
 
@@ -402,8 +408,18 @@ void status_strings() {
 
 }  // namespace
 
+// The tiling limit of the dense GEMM is handed to the library unchanged and
+// the previous setting comes back (negative values mean the default, -1).
+void small_gemm_limit() {
+  CHECK(fp8q_set_gemm_small_limit(0) == -1);
+  CHECK(fp8q_set_gemm_small_limit(int64_t(1) << 40) == 0);
+  CHECK(fp8q_set_gemm_small_limit(-7) == (int64_t(1) << 40));
+  CHECK(fp8q_set_gemm_small_limit(-1) == -1);
+}
+
 int main() {
   device_check();
+  small_gemm_limit();
   quantizers();
   gemms();
   moe_glue();

@@ -6,7 +6,9 @@ output the GPU value must be the RNE rounding of some float32 within that
 tolerance.  Operands are quantized by the oracle on the host and the same
 codes are given to both sides.
 
-Shapes: the tiny linear (every element), ragged M/N/K and small cases, the
+Shapes: the tiny linear (every element), ragged M/N/K and small cases (each
+on both tilings of the dense float32-grade GEMM: 32 x 32 split-K tiles and
+256-wide tiles, chosen with fp8q_set_gemm_small_limit), the
 dense expert up-projection 4096 x 4096 x 7168 (sampled elements and full
 rows), the MoE grouped GEMM with an empty expert, and the Wgrad 2048 x 7168
 over 16384 tokens (sampled).  Closed forms: selector weights give an exactly
@@ -45,6 +47,16 @@ def _accept(c_dev, c_ref, s_ref, what):
                              f"gpu {gotv[tuple(i)]!r} oracle {c_ref[tuple(i)]!r} S {s_ref[tuple(i)]!r}")
 
 
+@pytest.fixture(params=["split_k_32x32", "tiles_256"])
+def tiling(request):
+    """Runs the test with the dense float32-grade GEMM forced onto one tiling:
+    32 x 32 output tiles with the K blocks split over four waves, or 256-wide
+    tiles over the whole of K; the library default is restored afterwards."""
+    prev = fp8q.set_gemm_small_limit(1 << 62 if request.param == "split_k_32x32" else 0)
+    yield request.param
+    fp8q.set_gemm_small_limit(prev)
+
+
 def _operands(a_bits, w_bits):
     a_c, a_s = Q.quantize_rows(a_bits)
     w_c, w_s = Q.quantize_blocks(w_bits)
@@ -56,10 +68,10 @@ def _run_dense(a_c, a_s, w_c, w_s, out_dtype):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_tiny_linear_every_element(out_dtype):
+def test_tiny_linear_every_element(out_dtype, tiling):
     d = synth.tiny_linear()
     a_c, a_s, w_c, w_s = _operands(d["a"], d["w"])
-    say(f"[gemm] tiny linear 128x256x512 {out_dtype}")
+    say(f"[gemm] tiny linear 128x256x512 {out_dtype} {tiling}")
     c = _run_dense(a_c, a_s, w_c, w_s, out_dtype)
     ref, s = G.gemm(a_c, a_s, w_c, w_s)
     _accept(c, ref, s, "tiny linear")
@@ -68,29 +80,57 @@ def test_tiny_linear_every_element(out_dtype):
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (3, 5, 256), (17, 130, 384), (300, 202, 640),
                                    (256, 256, 1024), (513, 257, 128), (64, 1000, 256)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_ragged_shapes(m, n, k, out_dtype):
+def test_ragged_shapes(m, n, k, out_dtype, tiling):
     rng = np.random.default_rng(m * 31 + n * 7 + k)
     a = synth.bf16_rne((rng.standard_normal((m, k)) * np.exp2(rng.integers(-3, 4, (m, k)))).astype(np.float32))
     w = synth.bf16_rne((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
     a_c, a_s, w_c, w_s = _operands(a, w)
-    say(f"[gemm] ragged {m}x{n}x{k} {out_dtype}")
+    say(f"[gemm] ragged {m}x{n}x{k} {out_dtype} {tiling}")
     c = _run_dense(a_c, a_s, w_c, w_s, out_dtype)
     ref, s = G.gemm(a_c, a_s, w_c, w_s)
     _accept(c, ref, s, f"ragged {m}x{n}x{k}")
 
 
-def test_output_row_stride_and_untouched_padding():
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_output_row_stride_and_untouched_padding(out_dtype, tiling):
     d = synth.tiny_linear()
     a_c, a_s, w_c, w_s = _operands(d["a"], d["w"])
-    out = torch.full((128, 264), float("nan"), dtype=torch.float32, device="cuda:0")
-    say("[gemm] strided output")
-    fp8q.gemm(dev(a_c), dev(a_s), dev(w_c), dev(w_s), out=out[:, :256])
+    # a row stride of 262 elements is not a multiple of 4: element-wise stores
+    for ld in (264, 262):
+        out = torch.full((128, ld), float("nan"), dtype=out_dtype, device="cuda:0")
+        say(f"[gemm] strided output ld={ld} {out_dtype} {tiling}")
+        fp8q.gemm(dev(a_c), dev(a_s), dev(w_c), dev(w_s), out=out[:, :256])
+        ref, s = G.gemm(a_c, a_s, w_c, w_s)
+        _accept(out[:, :256], ref, s, f"strided output ld={ld}")
+        assert torch.isnan(out[:, 256:]).all()
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_mid_size_every_element(out_dtype, tiling):
+    """1000 x 1500 x 2560 (ragged in M and N; 20 K blocks, five per wave of
+    the split-K tiling), activations with 0.1% outliers x100 as in the dense
+    up-projection: every element against the oracle, and a second launch
+    bit-identical to the first (the split-K sum has a fixed order)."""
+    rng = np.random.default_rng(11)
+    m, n, k = 1000, 1500, 2560
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    hit = rng.choice(m * k, size=m * k // 1000, replace=False)
+    a.reshape(-1)[hit] *= np.float32(100.0)
+    a = synth.bf16_rne(a)
+    w = synth.bf16_rne((rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    a_c, a_s, w_c, w_s = _operands(a, w)
+    say(f"[gemm] mid size {m}x{n}x{k} {out_dtype} {tiling}")
+    ops = (dev(a_c), dev(a_s), dev(w_c), dev(w_s))
+    c = fp8q.gemm(*ops, out_dtype=out_dtype)
     ref, s = G.gemm(a_c, a_s, w_c, w_s)
-    _accept(out[:, :256], ref, s, "strided output")
-    assert torch.isnan(out[:, 256:]).all()
+    _accept(c, ref, s, f"mid size {tiling}")
+    c2 = fp8q.gemm(*ops, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16) if out_dtype == torch.bfloat16 else c.view(torch.int32),
+                       c2.view(torch.int16) if out_dtype == torch.bfloat16 else c2.view(torch.int32))
 
 
-def test_selector_weights_are_exact():
+def test_selector_weights_are_exact(tiling):
     """One nonzero weight code (+-1.0) per row per 128-block: C is a sum of
     K/128 scaled activation values, exactly computable; with power-of-two
     scales every term is exact in float32 and so is the GPU result."""
@@ -105,13 +145,13 @@ def test_selector_weights_are_exact():
         for b in range(k // 128):
             w_c[j, b * 128 + rng.integers(0, 128)] = 0x38 | (0x80 * rng.integers(0, 2))
     w_s = np.exp2(rng.integers(-2, 3, (2, k // 128))).astype(np.float32)
-    say("[gemm] selector weights")
+    say(f"[gemm] selector weights {tiling}")
     c = host(_run_dense(a_c, a_s, w_c, w_s, torch.float32)).astype(np.float64)
     ref, _ = G.gemm(a_c, a_s, w_c, w_s)
     assert np.array_equal(c, ref)
 
 
-def test_zero_scales_and_k_zero():
+def test_zero_scales_and_k_zero(tiling):
     d = synth.tiny_linear()
     a_c, a_s, w_c, w_s = _operands(d["a"], d["w"])
     a_s = a_s.copy()
@@ -241,16 +281,24 @@ def test_grouped_offsets_past_rows_cap_are_clamped():
 
 
 def test_grouped_equals_dense_per_group():
+    """The grouped GEMM and the dense GEMM on 256-wide tiles run the same K
+    loop, so each group's rows are bit-identical to a dense call on them (the
+    32 x 32 split-K tiling sums in another order and is held to the oracle
+    instead, above)."""
     d, cases = _grouped_case(tokens=256, hidden=256, inter=128, with_down=False)
     a_c, a_s, wc, ws = cases[0]
     offs = d["offsets"]
     say("[gemm] grouped == dense per group")
     cg = host(fp8q.grouped_gemm(dev(a_c), dev(a_s), dev(offs), dev(wc), dev(ws), out_dtype=torch.float32))
-    for gi in range(len(offs) - 1):
-        lo, hi = int(offs[gi]), int(offs[gi + 1])
-        if hi > lo:
-            cd = host(_run_dense(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], torch.float32))
-            assert np.array_equal(cg[lo:hi], cd), gi
+    prev = fp8q.set_gemm_small_limit(0)
+    try:
+        for gi in range(len(offs) - 1):
+            lo, hi = int(offs[gi]), int(offs[gi + 1])
+            if hi > lo:
+                cd = host(_run_dense(a_c[lo:hi], a_s[lo:hi], wc[gi], ws[gi], torch.float32))
+                assert np.array_equal(cg[lo:hi], cd), gi
+    finally:
+        fp8q.set_gemm_small_limit(prev)
 
 
 def _wgrad_operands(dy_bits, x_bits):

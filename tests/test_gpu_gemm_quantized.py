@@ -11,8 +11,10 @@ Checks:
   tile at small and ragged shapes and for whole sampled rows of the dense
   up-projection 4096 x 4096 x 7168, in both scale modes;
 * the fusion changes nothing: the codes and scales are bit-identical to
-  fp8q.gemm(BF16 out) followed by fp8q.quantize_act, in all three
-  accumulation forms, at the full dense size.
+  fp8q.gemm(BF16 out) on 256-wide tiles (the tiling the fused kernel has)
+  followed by fp8q.quantize_act, in every accumulation form, at the full
+  dense size and at 333 x 520 x 256, a size the float32-grade fp8q.gemm
+  would otherwise run on 32 x 32 split-K tiles.
 """
 
 import numpy as np
@@ -111,7 +113,11 @@ def test_fused_equals_gemm_then_quantize(acc):
         for out_mode in ("free", "pow2"):
             say(f"[gemm-q] fused vs unfused {m}x{n}x{k} acc={acc} out={out_mode}")
             codes, scales = fp8q.gemm_quantized(ac, as_, wc, ws, scale_mode=out_mode, acc=acc)
-            c = fp8q.gemm(ac, as_, wc, ws, out_dtype=torch.bfloat16, acc=acc)
+            prev = fp8q.set_gemm_small_limit(0)
+            try:
+                c = fp8q.gemm(ac, as_, wc, ws, out_dtype=torch.bfloat16, acc=acc)
+            finally:
+                fp8q.set_gemm_small_limit(prev)
             want_c, want_s = fp8q.quantize_act(c, scale_mode=out_mode)
             assert_codes_equal(host_codes(codes), host_codes(want_c), "fused codes")
             assert_scales_equal(host(scales), host(want_s), "fused scales")
