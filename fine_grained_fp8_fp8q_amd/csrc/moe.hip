@@ -84,18 +84,51 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return (g * sg) * u;
 }
 
+// The same value for gates g >= -64 in fewer instructions.  log2(e) is split
+// as c1 + (log2(e) - c1) with c1 = 47274 / 2^15, its rounding to 16
+// significant bits, so g * c1 is exact for every BF16 g (8 significant
+// bits): e^-g = 2^(-g c1) * e^(-g k), k = 1 - c1 ln 2 = 4.888e-6, is one
+// hardware exp2 of an exact argument times a factor within 3.2e-4 of 1,
+// taken to first order by one fused multiply-add (the dropped second-order
+// term is below 0.83 * 2^-24 relative for |g| <= 64).  sigma(g) =
+// 1 / (1 + e^-g) needs no case split: for g in [-64, 0) e^-g stays below
+// 2^93, and for large positive g it vanishes and 1 + e^-g is 1.
+__device__ __forceinline__ float swiglu_direct(float g, float u) {
+  constexpr float c1 = 47274.0f / 32768.0f;
+  constexpr float k = 4.8884954e-06f;  // RN32(1 - c1 ln 2)
+  const float e1 = __builtin_amdgcn_exp2f(g * -c1);
+  const float e = __builtin_fmaf(-(g * k), e1, e1);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  return (g * r) * u;
+}
+
+// Whether any of eight BF16 gates lies below -64: as unsigned 16-bit
+// patterns those are the ones above 0xC280 (the pattern of -64; NaN
+// patterns count too, and take the general path).
+__device__ __forceinline__ bool gate_below_m64(uint4 g) {
+  const uint32_t m = pk_max_u16(pk_max_u16(g.x, g.y), pk_max_u16(g.z, g.w));
+  return max(m & 0xFFFFu, m >> 16) > 0xC280u;
+}
+
 // Eight (gate, up) BF16 pairs -> eight BF16 SwiGLU values in chunk layout,
 // each rounded to nearest even by the hardware convert (v_cvt_pk_bf16_f32,
-// two values per instruction).
+// two values per instruction).  DIRECT: every gate is at least -64.
 typedef __bf16 sw_v2bf __attribute__((ext_vector_type(2)));
+template <bool DIRECT>
 __device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
   const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
   const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
   uint32_t y[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = swiglu(bf16_lo(gw[i]), bf16_lo(uw[i]));
-    const float hi = swiglu(bf16_hi(gw[i]), bf16_hi(uw[i]));
+    float lo, hi;
+    if constexpr (DIRECT) {
+      lo = swiglu_direct(bf16_lo(gw[i]), bf16_lo(uw[i]));
+      hi = swiglu_direct(bf16_hi(gw[i]), bf16_hi(uw[i]));
+    } else {
+      lo = swiglu(bf16_lo(gw[i]), bf16_lo(uw[i]));
+      hi = swiglu(bf16_hi(gw[i]), bf16_hi(uw[i]));
+    }
     y[i] = __builtin_bit_cast(uint32_t, sw_v2bf{(__bf16)lo, (__bf16)hi});
   }
   return make_uint4(y[0], y[1], y[2], y[3]);
@@ -169,7 +202,10 @@ __global__ __launch_bounds__(256) void swiglu_quant_kernel(const uint16_t* __res
     const uint32_t nbase = base + step;
     if (nbase < (uint32_t)ntiles) fetch(nbase, nxt);  // (wave-uniform)
     const int cb = cur.col >> 7;
-    const uint4 y = swiglu8(cur.g, cur.u);
+    // the general form only where a gate of this wave's chunks is below -64
+    // (wave-uniform branch)
+    const uint4 y = __builtin_amdgcn_ballot_w64(gate_below_m64(cur.g)) == 0 ? swiglu8<true>(cur.g, cur.u)
+                                                                          : swiglu8<false>(cur.g, cur.u);
     quant_store<POW2>(y, cur.full, cur.valid, cur.nvalid, codes + (int64_t)cur.row * ldc + cur.col,
                       scales + (int64_t)cur.row * nb + cb, sub);
     if constexpr (CACHE) {

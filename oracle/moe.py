@@ -20,8 +20,8 @@ Readings taken where the pages are silent:
 * The quantized value is the BF16 rounding (nearest, ties to even) of the
   exact SwiGLU value: the tensor an unfused SwiGLU would store in BF16 for
   the quantizer to read.  The GPU forms the value in float32 (hardware exp2
-  and reciprocal, one ulp each), whose relative error is below
-  ``swiglu_rel_error_bound()`` (about 2^-20.7); where the exact value lies
+  and reciprocal, one ulp each) in one of two ways, whose relative errors
+  are both below ``swiglu_rel_error_bound()`` (about 2^-20.5); where the exact value lies
   within BAND_REL = 2^-19 (relative) of the midpoint between two BF16 numbers
   either neighbour is accepted (``swiglu_accept``); everything else is
   compared bit for bit.
@@ -45,9 +45,42 @@ BAND_ABS = 2.0 ** -140  # float32 subnormal results carry absolute errors
 
 
 def swiglu_rel_error_bound(exp2_ulp=1.0, rcp_ulp=1.0):
-    """First-order bound on |y32 - y| / |y| for the float32 SwiGLU the GPU
-    forms, composed from the error of each step (u = 2^-24,
-    the float32 unit roundoff):
+    """Bound on |y32 - y| / |y| for both float32 forms of the SwiGLU the GPU
+    takes (the larger of the two bounds below); the band BAND_REL must
+    contain it."""
+    return max(swiglu_rel_error_bound_general(exp2_ulp, rcp_ulp),
+               swiglu_rel_error_bound_direct(exp2_ulp, rcp_ulp))
+
+
+def swiglu_rel_error_bound_direct(exp2_ulp=1.0, rcp_ulp=1.0, gate_min=-64.0):
+    """First-order bound on |y32 - y| / |y| for the form the GPU takes when
+    every gate of a chunk is at least ``gate_min`` (u = 2^-24):
+
+    * e^-g = 2^(-g c1) e^(-g k), c1 = 47274 / 2^15 (log2(e) to 16
+      significant bits, so g c1 is exact for a BF16 g) and
+      k = 1 - c1 ln 2 = 4.8885e-6 carried as RN32(k): the hardware exp2 of
+      the exact argument (exp2_ulp ulp, relative 2u * exp2_ulp) times
+      1 - g k by one fused multiply-add (one rounding, u), dropping the
+      second-order term (g k)^2 / 2 (relative, at most 0.83u for
+      |g| <= 64); g * RN32(k) is off by at most 2u relative, which moves
+      1 - g k by less than 2u * 3.2e-4:
+      e_e = 2u * exp2_ulp + u + (g_max k)^2 / 2 + 2u * g_max k;
+    * 1 + e^-g rounds (u) and carries e's error scaled by e / (1 + e) <= 1,
+      the hardware reciprocal adds rcp_ulp ulp (2u * rcp_ulp):
+      e_r = u + e_e + 2u * rcp_ulp;
+    * g * r and (g * r) * up: two more roundings, 2u.
+    """
+    u = 2.0 ** -24
+    gk = abs(gate_min) * 4.888495152143634e-6
+    e_e = 2 * u * exp2_ulp + u + gk * gk / 2 + 2 * u * gk
+    e_r = u + e_e + 2 * u * rcp_ulp
+    return e_r + 2 * u
+
+
+def swiglu_rel_error_bound_general(exp2_ulp=1.0, rcp_ulp=1.0):
+    """First-order bound on |y32 - y| / |y| for the form the GPU takes for
+    any gate (chunks with a gate below -64), composed from the error of
+    each step (u = 2^-24, the float32 unit roundoff):
 
     * exponent reduction x log2(e) = n + f with log2(e) carried as
       RN32(log2 e) + RN32(remainder) and two fused multiply-adds: |df| <= 2u

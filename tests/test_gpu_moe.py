@@ -13,8 +13,9 @@ midpoint may take either neighbour); tiles with no such element are also
 compared directly with the oracle's quantization.  The optional cache of the
 input is bit-exact against the oracle's 1x128 quantization of the input and
 against fp8q.quantize_act.  Shapes: ragged inter (1, 100, 130), multiples of
-128, a strided input, special gate values, and the MoE workload's
-[3773, 2 x 2048] up-projection output shape in full.
+128, a strided input, special gate values, gate ranges that put the kernel
+in each of its two float32 forms, and the MoE workload's [3773, 2 x 2048]
+up-projection output shape in full.
 """
 
 import numpy as np
@@ -23,6 +24,7 @@ import torch
 
 import fine_grained_fp8_fp8q_amd as fp8q
 from oracle import moe, quantize as Q
+from oracle.e4m3 import bf16_bits_to_f32
 import synth
 from tests.gpu_util import (assert_codes_equal, assert_scales_equal, dev, dev_bf16, host, host_codes,
                             need_gpu, say)
@@ -144,6 +146,30 @@ def test_swiglu_strided_and_special_values():
     for mode in ("free", "pow2"):
         say(f"[moe] swiglu special values, strided input, {mode}")
         _check_swiglu(x, mode, f"swiglu special {mode}", x_dev=xd, cache=True)
+
+
+def test_swiglu_gate_ranges_of_both_forms():
+    """The kernel forms a chunk's values in one of two float32 ways, chosen
+    per wave: the direct one when every gate of the wave's chunks is at
+    least -64, the general one otherwise.  Rows 0-31 hold gates in
+    [-64, -40] (the direct form's largest e^-g, -64 itself included),
+    rows 32-63 gates in [40, 1000]; rows 64-127 are the same draws with a
+    single gate in [-104, -64) planted in every fourth tile, so those waves
+    take the general form for all four of their tiles."""
+    rng = np.random.default_rng(21)
+    inter = 512
+    g = np.concatenate([rng.uniform(-64, -40, (32, inter)), rng.uniform(40, 1000, (32, inter))])
+    g[0, :4] = [-64.0, -63.75, -40.0, -50.5]
+    g = np.concatenate([g, g]).astype(np.float32)
+    for r in range(64, 128):
+        g[r, 128 * (r % 4) + (r * 7) % 128] = -rng.uniform(64.5, 104)
+    u = (rng.standard_normal((128, inter)) * np.exp2(rng.integers(-2, 3, (128, 1)))).astype(np.float32)
+    x = synth.bf16_rne(np.concatenate([g, u], axis=1))
+    gv = bf16_bits_to_f32(x[:, :inter])
+    assert gv[:64].min() >= -64 and (gv[64:] < -64).sum() == 64
+    for mode in ("free", "pow2"):
+        say(f"[moe] swiglu gate ranges of both forms, {mode}")
+        _check_swiglu(x, mode, f"swiglu gate ranges {mode}", cache=True)
 
 
 @pytest.mark.parametrize("mode", ["free", "pow2"])

@@ -159,15 +159,69 @@ def _swiglu_f32(g, u, k_exp, k_rcp):
     return _f32(_f32(g.astype(np.float64) * sg).astype(np.float64) * u)
 
 
+def _swiglu_f32_direct(g, u, k_exp, k_rcp):
+    """The GPU's float32 SwiGLU for gates >= -64, emulated step by step:
+    g times c1 = 47274 / 2^15 (exact in float32 for a BF16 g; checked),
+    exp2 correctly rounded and pushed k_exp ulps, the first-order factor
+    1 - g * RN32(k) applied by one fused multiply-add, 1 + e, the reciprocal
+    correctly rounded and pushed k_rcp ulps, then two products."""
+    g = _f32(g)
+    u = _f32(u)
+    c1 = np.float32(47274.0 / 32768.0)
+    k = np.float32(4.8884954e-06)
+    arg64 = -g.astype(np.float64) * np.float64(c1)
+    arg = _f32(arg64)
+    assert np.array_equal(arg.astype(np.float64), arg64)  # the product is exact
+    e1 = _ulp_push(_f32(np.exp2(arg.astype(np.float64))), k_exp)
+    h = _f32(g.astype(np.float64) * np.float64(k))
+    e = _f32(e1.astype(np.float64) - h.astype(np.float64) * e1.astype(np.float64))
+    r = _ulp_push(_f32(1.0 / _f32(1.0 + e.astype(np.float64)).astype(np.float64)), k_rcp)
+    return _f32(_f32(g.astype(np.float64) * r).astype(np.float64) * u)
+
+
+def test_swiglu_direct_form_error_bound():
+    """The bound of the form taken when every gate is at least -64
+    (oracle.moe.swiglu_rel_error_bound_direct) against the emulation above
+    on 200,000 BF16 pairs with gates over [-64, 64] and a dense core, the
+    hardware exp2 and reciprocal pushed one ulp either way; the split
+    constants are what they claim (c1 has 16 significant bits and is
+    log2(e) to that precision, RN32(k) is the float32 rounding of
+    1 - c1 ln 2), and the bound is inside the overall one and the band."""
+    c1 = 47274.0 / 32768.0
+    assert 47274 < 2 ** 16 and abs(c1 - 1 / np.log(2)) < 2.0 ** -16
+    assert np.float32(4.8884954e-06) == np.float32(1.0 - c1 * np.log(2.0))
+    bound = moe.swiglu_rel_error_bound_direct()
+    assert bound <= moe.swiglu_rel_error_bound() < moe.BAND_REL / 2
+    rng = np.random.default_rng(12)
+    g = np.concatenate([rng.uniform(-64, 64, 150000), rng.uniform(-64, -40, 25000),
+                        rng.standard_normal(25000) * 1.7]).astype(np.float32)
+    ub = rng.standard_normal(g.size).astype(np.float32)
+    gb = e4m3.bf16_bits_to_f32(_bits(g)).astype(np.float64)
+    assert gb.min() >= -64
+    uv = e4m3.bf16_bits_to_f32(_bits(ub)).astype(np.float64)
+    exact = moe.silu(gb) * uv
+    worst = 0.0
+    for k_exp in (-1, 0, 1):
+        for k_rcp in (-1, 0, 1):
+            y = _swiglu_f32_direct(gb, uv, k_exp, k_rcp).astype(np.float64)
+            err = np.abs(y - exact)
+            ok = err <= bound * np.abs(exact) + moe.BAND_ABS
+            assert ok.all(), (k_exp, k_rcp, gb[~ok][:3], (err / np.abs(exact))[~ok][:3])
+            normal = np.abs(exact) > 2.0 ** -100
+            worst = max(worst, float((err[normal] / np.abs(exact[normal])).max()))
+    assert worst > bound / 8, (worst, bound)
+
+
 def test_swiglu_error_bound_holds_and_sits_inside_the_band():
-    """The composed bound (oracle.moe.swiglu_rel_error_bound) against an
+    """The composed bound of the general form
+    (oracle.moe.swiglu_rel_error_bound_general) against an
     emulation of the kernel's float32 arithmetic on 200,000 BF16 (gate, up)
     pairs spread over gates in [-40, 40] (and tails to -104), with the
     hardware exp2 and reciprocal results pushed one ulp up or down: every
     emulated result is within the bound of the exact value, and the bound is
     inside the acceptance band BAND_REL."""
-    bound = moe.swiglu_rel_error_bound()
-    assert bound < moe.BAND_REL / 2
+    bound = moe.swiglu_rel_error_bound_general()
+    assert bound <= moe.swiglu_rel_error_bound() < moe.BAND_REL / 2
     rng = np.random.default_rng(11)
     g = np.concatenate([rng.uniform(-40, 40, 150000), rng.uniform(-104, -40, 25000),
                         rng.standard_normal(25000) * 1.7]).astype(np.float32)
