@@ -62,9 +62,9 @@ GEMM_MIN_BYTES = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 
 # when csrc/gemm.hip no longer hashes to `source_sha256` the bench reports
 # traffic null.
 GEMM_TRAFFIC = {"bytes": 216190000,
-                "source_sha256": "a19cc29ec6707f5cb26530d1b19464ab9a58461561f37cec286ec4e3eddf38db",
-                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,415.6 KiB x 2.000 "
-                           "+ WRITE_SIZE 34,305.0 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
+                "source_sha256": "5d0102877e6675f5b3e375937b8be0ce3ee28db1d42af65db226de7d529d2918",
+                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,415.0 KiB x 2.000 "
+                           "+ WRITE_SIZE 34,307.3 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
 
 
 def parse():
