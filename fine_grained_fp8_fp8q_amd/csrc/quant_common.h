@@ -96,15 +96,28 @@ struct TileScale {
 
 constexpr uint32_t kMarksteinMinAmaxBits = 37u << 7;  // BF16 pattern of 2^-90
 
+// The scale and the reciprocal of the divisor take no IEEE division either:
+// s = RN32(amax / 448) is the same Markstein correction of amax * RN32(1/448),
+// and RN32(1 / div) is one Newton step, fma(fma(-div, y, 1), y, y), from the
+// hardware reciprocal y.  For every nonzero finite BF16 amax the first equals
+// the IEEE quotient, and the second equals the IEEE reciprocal of each
+// divisor a tile can have (s, or s * 2^64 for a tiny amax) from every y
+// within 2 ulps of it (the hardware's is documented within 1); both are
+// checked on the host over all 32,639 such amax.
 __device__ __forceinline__ TileScale tile_scale_free(uint32_t amax_bits) {
   TileScale t;
-  float amax = __uint_as_float(amax_bits << 16);
-  float s = amax / 448.0f;  // IEEE division (no fast-math)
+  const float amax = __uint_as_float(amax_bits << 16);
+  constexpr float kInv448 = 1.0f / 448.0f;  // RN32(1/448)
+  const float q0 = amax * kInv448;
+  const float s = __builtin_fmaf(__builtin_fmaf(-q0, 448.0f, amax), kInv448, q0);
   t.s = s;
   t.slow = amax_bits != 0 && amax_bits < kMarksteinMinAmaxBits;
   t.xscale = t.slow ? 0x1p64f : 1.0f;
-  t.div = amax_bits ? s * t.xscale : 1.0f;
-  t.mul = 1.0f / t.div;
+  const float div = s * t.xscale;
+  const float y = __builtin_amdgcn_rcpf(div);
+  const float r = __builtin_fmaf(__builtin_fmaf(-div, y, 1.0f), y, y);
+  t.div = amax_bits ? div : 1.0f;
+  t.mul = amax_bits ? r : 1.0f;
   t.neg_e = 0;
   return t;
 }

@@ -1,7 +1,8 @@
 /* Exhaustive host check of the quantizers' element quotient.
  *
  * The 1x128 / 128x128 quantizers form a tile's scale s = RN32(amax / 448)
- * with an IEEE division, and each element's quotient RN32(x / s) -- the
+ * and r = RN32(1 / s) (without divisions; scale_reciprocal_check.c shows both
+ * equal the IEEE results), and each element's quotient RN32(x / s) -- the
  * value the E4M3 rounding then reads -- with one Markstein correction of the
  * product by the rounded reciprocal (M. Markstein, "Computation of
  * elementary functions on the IBM RISC System/6000 processor", IBM J. Res.
