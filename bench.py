@@ -63,8 +63,8 @@ GEMM_MIN_BYTES = M * K + N * K + M * (K // 128) * 4 + (N // 128) * (K // 128) * 
 # traffic null.
 GEMM_TRAFFIC = {"bytes": 216190000,
                 "source_sha256": "5d0102877e6675f5b3e375937b8be0ce3ee28db1d42af65db226de7d529d2918",
-                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,415.0 KiB x 2.000 "
-                           "+ WRITE_SIZE 34,307.3 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
+                "profile": "profiles/bench_workloads_kernel_trace_and_hbm_traffic.md (FETCH_SIZE 88,416.8 KiB x 2.000 "
+                           "+ WRITE_SIZE 34,307.4 KiB per launch of gemm_bs_kernel<0, 1, 0, 0>)"}
 
 
 def parse():
