@@ -419,6 +419,11 @@ def moe(torch, fp8q, lib, clock, sp, reps):
         if cache:
             sbytes += rows * 2 * inter + rows * (2 * inter // 128) * 4
         out[name] = clock.stats(fs, reps, nbytes=sbytes)
+        # a bare 2:1 stream moving the same number of bytes (the kernel's mix
+        # is 4:1 reads to writes): the rate a plain stream of this size gets
+        ps = plain_stream(torch, clock, sp, sbytes // 3, reps, 2)
+        out[name]["plain_stream_same_bytes"] = ps
+        out[name]["frac_of_plain_stream"] = round(ps["batch_avg_us"] / out[name]["batch_avg_us"], 3)
     del sxs, sx0, cq, cs
 
     weights = {}
