@@ -20,7 +20,8 @@ namespace fp8q {
 // (1 KiB when they share a row).  The scales of a DPP row's four tiles are
 // worked out once, lane u of the row taking tile u, and broadcast back to
 // the row (row_newbcast): one scale computation per lane and iteration
-// instead of four (the free scale is two IEEE divisions).
+// instead of four (the free scale is a corrected quotient and a corrected
+// reciprocal, about 10 instructions).
 
 // Tile u's scale state, from lane u of each DPP row.
 template <bool POW2, int U>
